@@ -1,0 +1,448 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950) - Python binding.
+
+A thin ctypes layer over ``libpagedkv.so`` (C ABI in ``include/pagedkv.h``).
+Functions keep the C names; this module only marshals arguments.  torch is
+used for device memory and streams; every step of the computation runs in the
+library's host allocator or its HIP kernels.  There is no fallback: if the
+library is missing, importing this package fails.
+
+Build the library with ``python -m paged_kv_cache_263_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first: the library then binds to the HIP runtime torch loaded
+
+__all__ = [
+    "PagedKVError", "Pool", "KVCache", "LIB_PATH",
+    "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_incref", "kv_pool_free",
+    "kv_pool_refcount", "kv_pool_stats", "kv_pool_free_list",
+    "seq_create", "seq_append", "seq_append_batch", "seq_fork", "seq_share_prefix", "seq_free",
+    "seq_len", "seq_num_blocks", "block_table_build",
+    "paged_attn_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
+    "kv_cache_write", "kv_copy_blocks", "pkv_strerror", "pkv_last_error", "pkv_version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+_STATUS = {0: "OK", -1: "INVALID", -2: "OOM", -3: "STATE", -4: "UNSUPPORTED", -5: "HIP", -6: "WORKSPACE"}
+
+
+class PagedKVError(RuntimeError):
+    """A non-zero status from the library; ``code`` is its PKV_ERR_* name."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.code = _STATUS.get(status, str(status))
+        super().__init__(f"{self.code}: {message}")
+
+
+class pkv_copy(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_int32), ("dst", ctypes.c_int32), ("valid_tokens", ctypes.c_int32)]
+
+
+class pkv_stats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
+                ("refcount_sum", ctypes.c_int64), ("cow_count", ctypes.c_int64),
+                ("num_seqs", ctypes.c_int64), ("tokens", ctypes.c_int64), ("waste_tokens", ctypes.c_int64)]
+
+
+class pkv_cache(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+class pkv_attn_args(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("kv_lens", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32),
+                ("cu_q", ctypes.c_void_p), ("num_decode", ctypes.c_int32),
+                ("max_decode_kv_len", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_i32, _p, _pi32 = ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+_SIGNATURES = {
+    "kv_pool_create": (ctypes.c_int, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
+    "kv_pool_destroy": (None, [_p]),
+    "kv_pool_alloc": (ctypes.c_int, [_p, _i32, _pi32]),
+    "kv_pool_incref": (ctypes.c_int, [_p, _pi32, _i32]),
+    "kv_pool_free": (ctypes.c_int, [_p, _pi32, _i32]),
+    "kv_pool_refcount": (ctypes.c_int, [_p, _i32, _pi32]),
+    "kv_pool_stats": (ctypes.c_int, [_p, ctypes.POINTER(pkv_stats)]),
+    "kv_pool_free_list": (ctypes.c_int, [_p, _pi32, _i32, _pi32]),
+    "seq_create": (ctypes.c_int, [_p, _pi32]),
+    "seq_append": (ctypes.c_int, [_p, _i32, _i32, _pi32, ctypes.POINTER(pkv_copy), _pi32]),
+    "seq_append_batch": (ctypes.c_int, [_p, _pi32, _pi32, _i32, _pi32, ctypes.POINTER(pkv_copy), _pi32]),
+    "seq_fork": (ctypes.c_int, [_p, _i32, _pi32]),
+    "seq_share_prefix": (ctypes.c_int, [_p, _i32, _i32, _pi32]),
+    "seq_free": (ctypes.c_int, [_p, _i32]),
+    "seq_len": (ctypes.c_int, [_p, _i32, _pi32]),
+    "seq_num_blocks": (ctypes.c_int, [_p, _i32, _pi32]),
+    "block_table_build": (ctypes.c_int, [_p, _pi32, _i32, _i32, _pi32, _pi32]),
+    "paged_attn_workspace_size": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args),
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "paged_attn_decode": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args), _p]),
+    "paged_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args), _p]),
+    "kv_cache_write": (ctypes.c_int, [ctypes.POINTER(pkv_cache), _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32,
+                                      _p, _i32, _p, _p]),
+    "kv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_copy), _i32, _p]),
+    "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_int, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run: python -m paged_kv_cache_263_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PagedKVError(status, _lib.pkv_last_error().decode())
+
+
+def pkv_strerror(status: int) -> str:
+    return _lib.pkv_strerror(status).decode()
+
+
+def pkv_last_error() -> str:
+    return _lib.pkv_last_error().decode()
+
+
+def pkv_version() -> int:
+    return _lib.pkv_version()
+
+
+def _i32_array(values):
+    values = [int(v) for v in values]
+    return (ctypes.c_int32 * max(1, len(values)))(*values), len(values)
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+
+
+class Pool:
+    """Handle of a host block pool (metadata only); freed on garbage collection."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise PagedKVError(-1, "pool destroyed")
+        return self._h
+
+    def destroy(self):
+        if self._h is not None:
+            _lib.kv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def kv_pool_create(num_blocks: int, order=None, block_size: int = BLOCK_SIZE) -> Pool:
+    h = ctypes.c_void_p()
+    arr = None
+    if order is not None:
+        arr, n = _i32_array(order)
+        if n != num_blocks:
+            raise PagedKVError(-1, "order must list every block once")
+    _check(_lib.kv_pool_create(num_blocks, block_size, arr, ctypes.byref(h)))
+    return Pool(h)
+
+
+def kv_pool_destroy(pool: Pool) -> None:
+    pool.destroy()
+
+
+def kv_pool_alloc(pool: Pool, n: int) -> list:
+    out = (ctypes.c_int32 * max(1, n))()
+    _check(_lib.kv_pool_alloc(pool.handle, n, out))
+    return list(out[:n])
+
+
+def kv_pool_incref(pool: Pool, ids) -> None:
+    arr, n = _i32_array(ids)
+    _check(_lib.kv_pool_incref(pool.handle, arr, n))
+
+
+def kv_pool_free(pool: Pool, ids) -> None:
+    arr, n = _i32_array(ids)
+    _check(_lib.kv_pool_free(pool.handle, arr, n))
+
+
+def kv_pool_refcount(pool: Pool, block: int) -> int:
+    out = ctypes.c_int32()
+    _check(_lib.kv_pool_refcount(pool.handle, block, ctypes.byref(out)))
+    return out.value
+
+
+def kv_pool_stats(pool: Pool) -> dict:
+    s = pkv_stats()
+    _check(_lib.kv_pool_stats(pool.handle, ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in pkv_stats._fields_}
+
+
+def kv_pool_free_list(pool: Pool) -> list:
+    n = ctypes.c_int32()
+    cap = kv_pool_stats(pool)["num_blocks"]
+    out = (ctypes.c_int32 * max(1, cap))()
+    _check(_lib.kv_pool_free_list(pool.handle, out, cap, ctypes.byref(n)))
+    return list(out[: n.value])
+
+
+def seq_create(pool: Pool) -> int:
+    s = ctypes.c_int32()
+    _check(_lib.seq_create(pool.handle, ctypes.byref(s)))
+    return s.value
+
+
+def seq_append(pool: Pool, seq: int, n_tokens: int):
+    """Returns (slots, copies); copies is a list of (src, dst, valid_tokens)."""
+    slots = (ctypes.c_int32 * max(1, n_tokens))()
+    cp = pkv_copy()
+    nc = ctypes.c_int32()
+    _check(_lib.seq_append(pool.handle, seq, n_tokens, slots, ctypes.byref(cp), ctypes.byref(nc)))
+    return list(slots[:n_tokens]), [(cp.src, cp.dst, cp.valid_tokens)] if nc.value else []
+
+
+def seq_append_batch(pool: Pool, seqs, n_tokens, out_slots=None):
+    """Append n_tokens[i] tokens to seqs[i] for all i (all or nothing).
+
+    Returns (slots, copies).  ``out_slots`` may be a preallocated ctypes int32
+    array (or a CPU int32 tensor) of sum(n_tokens) entries, filled in place."""
+    sa, n = _i32_array(seqs)
+    na, _ = _i32_array(n_tokens)
+    total = sum(int(x) for x in n_tokens)
+    if out_slots is None:
+        buf = (ctypes.c_int32 * max(1, total))()
+        ptr = buf
+    elif isinstance(out_slots, torch.Tensor):
+        buf = out_slots
+        ptr = ctypes.cast(out_slots.data_ptr(), _pi32)
+    else:
+        buf = out_slots
+        ptr = out_slots
+    copies = (pkv_copy * max(1, n))()
+    nc = ctypes.c_int32()
+    _check(_lib.seq_append_batch(pool.handle, sa, na, n, ptr, copies, ctypes.byref(nc)))
+    cps = [(copies[i].src, copies[i].dst, copies[i].valid_tokens) for i in range(nc.value)]
+    if out_slots is None:
+        return list(buf[:total]), cps
+    return buf, cps
+
+
+def seq_fork(pool: Pool, parent: int) -> int:
+    c = ctypes.c_int32()
+    _check(_lib.seq_fork(pool.handle, parent, ctypes.byref(c)))
+    return c.value
+
+
+def seq_share_prefix(pool: Pool, src: int, n_tokens: int) -> int:
+    c = ctypes.c_int32()
+    _check(_lib.seq_share_prefix(pool.handle, src, n_tokens, ctypes.byref(c)))
+    return c.value
+
+
+def seq_free(pool: Pool, seq: int) -> None:
+    _check(_lib.seq_free(pool.handle, seq))
+
+
+def seq_len(pool: Pool, seq: int) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.seq_len(pool.handle, seq, ctypes.byref(n)))
+    return n.value
+
+
+def seq_num_blocks(pool: Pool, seq: int) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.seq_num_blocks(pool.handle, seq, ctypes.byref(n)))
+    return n.value
+
+
+def block_table_build(pool: Pool, seqs, max_blocks: int):
+    """Returns (table, lens) as CPU int32 tensors [n, max_blocks] and [n]."""
+    sa, n = _i32_array(seqs)
+    table = torch.empty((n, max_blocks), dtype=torch.int32)
+    lens = torch.empty((n,), dtype=torch.int32)
+    _check(_lib.block_table_build(pool.handle, sa, n, max_blocks, ctypes.cast(table.data_ptr(), _pi32),
+                                  ctypes.cast(lens.data_ptr(), _pi32)))
+    return table, lens
+
+
+# ---------------------------------------------------------------------------
+# device cache and kernels
+
+_DT = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}
+_QDT = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+_NAMES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+
+
+class KVCache:
+    """Device K/V pools (torch tensors owned by this object).
+
+    k_pool: [layers, num_blocks, kv_heads, 16, 128]; v_pool: [layers, num_blocks,
+    kv_heads, 128, 16] (token-minor inside a block); fp8 pools hold E4M3 codes
+    as uint8 with fp32 scales [layers, kv_heads] for K and V."""
+
+    def __init__(self, kv_dtype, num_layers: int, num_blocks: int, num_kv_heads: int, device="cuda",
+                 k_scale=None, v_scale=None, zero: bool = True):
+        self.kv_dtype = _NAMES.get(kv_dtype, kv_dtype)
+        self.num_layers, self.num_blocks, self.num_kv_heads = num_layers, num_blocks, num_kv_heads
+        dt = _DT[self.kv_dtype]
+        alloc = torch.zeros if zero else torch.empty
+        self.k_pool = alloc((num_layers, num_blocks, num_kv_heads, BLOCK_SIZE, HEAD_DIM), dtype=dt, device=device)
+        self.v_pool = alloc((num_layers, num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE), dtype=dt, device=device)
+        self.k_scale = self.v_scale = None
+        if self.kv_dtype == PKV_FP8_E4M3:
+            if k_scale is None or v_scale is None:
+                raise PagedKVError(-1, "fp8 cache needs k_scale and v_scale")
+            self.k_scale = torch.as_tensor(k_scale, dtype=torch.float32).reshape(num_layers, num_kv_heads).to(device)
+            self.v_scale = torch.as_tensor(v_scale, dtype=torch.float32).reshape(num_layers, num_kv_heads).to(device)
+        self._desc = pkv_cache(self.kv_dtype, num_layers, num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE,
+                               self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+                               self.k_scale.data_ptr() if self.k_scale is not None else None,
+                               self.v_scale.data_ptr() if self.v_scale is not None else None)
+
+    @property
+    def desc(self) -> pkv_cache:
+        return self._desc
+
+    @property
+    def value_dtype(self) -> torch.dtype:
+        return torch.float32 if self.kv_dtype == PKV_F32 else torch.bfloat16
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace,
+          cu_q=None, num_decode=0, max_decode_kv_len=0, max_q_len=0, total_q=0) -> pkv_attn_args:
+    if q.dtype not in _QDT:
+        raise PagedKVError(-4, f"query dtype {q.dtype}")
+    for t in (q, out, block_table, kv_lens):
+        if not t.is_contiguous():
+            raise PagedKVError(-1, "tensors must be contiguous")
+    if block_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise PagedKVError(-1, "block_table and kv_lens must be int32")
+    a = pkv_attn_args()
+    a.layer = layer
+    a.q_dtype = _QDT[q.dtype]
+    a.num_seqs = block_table.shape[0]
+    a.num_q_heads = q.shape[1]
+    a.q = q.data_ptr()
+    a.out = out.data_ptr()
+    a.block_table = block_table.data_ptr()
+    a.max_blocks = block_table.shape[1]
+    a.kv_lens = kv_lens.data_ptr()
+    a.max_kv_len = int(max_kv_len)
+    a.cu_q = cu_q.data_ptr() if cu_q is not None else None
+    a.num_decode = num_decode
+    a.max_decode_kv_len = int(max_decode_kv_len)
+    a.max_q_len = int(max_q_len)
+    a.total_q = int(total_q)
+    a.split_tokens = split_tokens
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def paged_attn_workspace_size(cache: KVCache, args: pkv_attn_args) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.paged_attn_workspace_size(ctypes.byref(cache.desc), ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def _with_workspace(cache, a, workspace, device):
+    if workspace is None:
+        need = paged_attn_workspace_size(cache, a)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+            a.workspace = workspace.data_ptr()
+            a.workspace_bytes = need
+    return workspace
+
+
+def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, out=None, layer: int = 0,
+                      split_tokens: int = 0, workspace=None, stream=None):
+    """q [rows, Hq, 128] -> out [rows, Hq, 128] (q's dtype)."""
+    if out is None:
+        out = torch.empty_like(q)
+    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace)
+    keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841 (alive until enqueued)
+    _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_kv_len: int, num_decode: int,
+                             max_q_len: int, out=None, layer: int = 0, max_decode_kv_len: int = 0,
+                             split_tokens: int = 0, workspace=None, stream=None):
+    """q [total_q, Hq, 128]; rows 0..num_decode-1 are decode rows (cu_q[i] = i)."""
+    if out is None:
+        out = torch.empty_like(q)
+    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace, cu_q=cu_q,
+              num_decode=num_decode, max_decode_kv_len=max_decode_kv_len, max_q_len=max_q_len,
+              total_q=q.shape[0])
+    keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841
+    _check(_lib.paged_attn_prefill_chunk(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def kv_cache_write(cache: KVCache, k_new, v_new, slots, layer: int = 0, rows=None, positions=None,
+                   block_table=None, kv_lens=None, stream=None) -> None:
+    """Write [n, Hkv, 128] K/V values to their slots (device int32 [n])."""
+    if k_new.dtype != cache.value_dtype or v_new.dtype != cache.value_dtype:
+        raise PagedKVError(-4, f"values must be {cache.value_dtype}")
+    for t in (k_new, v_new, slots):
+        if not t.is_contiguous():
+            raise PagedKVError(-1, "tensors must be contiguous")
+    n = int(slots.numel())
+    num_rows = int(block_table.shape[0]) if block_table is not None else 0
+    max_blocks = int(block_table.shape[1]) if block_table is not None else 0
+    _check(_lib.kv_cache_write(ctypes.byref(cache.desc), layer, n,
+                               PKV_F32 if cache.value_dtype == torch.float32 else PKV_BF16,
+                               _ptr(k_new), _ptr(v_new), _ptr(slots), _ptr(rows), _ptr(positions), num_rows,
+                               _ptr(block_table), max_blocks, _ptr(kv_lens), _stream(stream)))
+
+
+def kv_copy_blocks(cache: KVCache, copies, stream=None) -> None:
+    """copies: iterable of (src, dst, valid_tokens)."""
+    copies = list(copies)
+    arr = (pkv_copy * max(1, len(copies)))(*[pkv_copy(*c) for c in copies])
+    _check(_lib.kv_copy_blocks(ctypes.byref(cache.desc), arr, len(copies), _stream(stream)))

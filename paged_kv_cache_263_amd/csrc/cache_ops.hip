@@ -1,0 +1,169 @@
+// Writes into the paged cache: new tokens' K/V to their slots (with fp8
+// quantisation on write), and whole-block copies for copy-on-write.
+//
+// A new block is needed every 16 tokens and a token's slot comes from the
+// host allocator ([P3] "PagedAttention block management", item (c)); a
+// sequence that must write into a shared block first gets its own copy ([P2]
+// "Sharing, and what makes a prefix reusable"; [P3] item (g)).  The fp8 cache
+// stores one byte per element ([P2] "Quantising the cache"): code = E4M3
+// round-to-nearest-even of fp32(x / scale), saturating at +-448.
+#include "device.h"
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+struct WriteParams {
+    const void* k_new;     // [n][hkv][128]
+    const void* v_new;
+    const int32_t* slots;  // [n]
+    const int32_t* rows;   // [n] or null
+    const int32_t* positions;
+    int32_t* table;        // [num_rows][max_blocks] or null
+    int32_t* kv_lens;      // [num_rows]
+    void* k_pool;          // this layer
+    void* v_pool;
+    const float* k_scale;  // this layer [hkv]
+    const float* v_scale;
+    int32_t n, hkv, num_blocks, num_rows, max_blocks;
+};
+
+template <int KV>
+__global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
+    const int i = blockIdx.x;
+    const int slot = p.slots[i];
+    const bool slot_ok = slot >= 0 && slot < p.num_blocks * kBS;
+    if (threadIdx.x == 0 && p.table && slot_ok) {
+        const int row = p.rows[i];
+        const int pos = p.positions[i];
+        if (row >= 0 && row < p.num_rows && pos >= 0 && pos / kBS < p.max_blocks) {
+            p.table[static_cast<int64_t>(row) * p.max_blocks + pos / kBS] = slot / kBS;
+            if (i == p.n - 1 || p.rows[i + 1] != row) p.kv_lens[row] = pos + 1;
+        }
+    }
+    if (!slot_ok) return;
+    const int blk = slot / kBS;
+    const int o = slot % kBS;
+    const int count = p.hkv * kD;
+    for (int e = threadIdx.x; e < count; e += blockDim.x) {
+        const int h = e / kD;
+        const int d = e % kD;
+        const int64_t src = static_cast<int64_t>(i) * count + e;
+        const int64_t tile = (static_cast<int64_t>(blk) * p.hkv + h) * kTile;
+        const int64_t kdst = tile + o * kD + d;   // K tile [16][128]
+        const int64_t vdst = tile + d * kBS + o;  // V tile [128][16]
+        if constexpr (KV == PKV_F32) {
+            static_cast<float*>(p.k_pool)[kdst] = static_cast<const float*>(p.k_new)[src];
+            static_cast<float*>(p.v_pool)[vdst] = static_cast<const float*>(p.v_new)[src];
+        } else if constexpr (KV == PKV_BF16) {
+            static_cast<uint16_t*>(p.k_pool)[kdst] = static_cast<const uint16_t*>(p.k_new)[src];
+            static_cast<uint16_t*>(p.v_pool)[vdst] = static_cast<const uint16_t*>(p.v_new)[src];
+        } else {
+            const float xk = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.k_new)[src]) << 16);
+            const float xv = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.v_new)[src]) << 16);
+            static_cast<uint8_t*>(p.k_pool)[kdst] = static_cast<uint8_t>(e4m3_code_rne(xk / p.k_scale[h]));
+            static_cast<uint8_t*>(p.v_pool)[vdst] = static_cast<uint8_t>(e4m3_code_rne(xv / p.v_scale[h]));
+        }
+    }
+}
+
+constexpr int kCopyBatch = 32;
+struct CopyParams {
+    int32_t src[kCopyBatch];
+    int32_t dst[kCopyBatch];
+    char* k_pool;
+    char* v_pool;
+    int64_t block_bytes;  // one (layer, block): hkv * 16 * 128 * elt
+    int64_t layer_bytes;  // one layer of one pool
+};
+
+// blockIdx: x = copy, y = layer, z = 0 (K) / 1 (V).  Copies one block of one
+// layer of one pool with 16-byte accesses (block_bytes is a multiple of 512).
+__global__ __launch_bounds__(256) void kv_copy_kernel(const CopyParams p) {
+    char* base = (blockIdx.z == 0 ? p.k_pool : p.v_pool) + blockIdx.y * p.layer_bytes;
+    const u32x4_t* s = reinterpret_cast<const u32x4_t*>(base + p.src[blockIdx.x] * p.block_bytes);
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(base + p.dst[blockIdx.x] * p.block_bytes);
+    const int64_t n = p.block_bytes / 16;
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) d[e] = s[e];
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" {
+
+int kv_cache_write(const pkv_cache* c, int32_t layer, int32_t n_tokens, int32_t val_dtype, const void* k_new,
+                   const void* v_new, const int32_t* slots, const int32_t* rows, const int32_t* positions,
+                   int32_t num_rows, int32_t* block_table, int32_t max_blocks, int32_t* kv_lens, void* stream) {
+    int st = pkv::check_cache(c);
+    if (st) return st;
+    if (layer < 0 || layer >= c->num_layers) return fail(PKV_ERR_INVALID, "layer %d out of range", layer);
+    if (n_tokens < 0) return fail(PKV_ERR_INVALID, "negative token count");
+    const int want = c->kv_dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+    if (val_dtype != want) return fail(PKV_ERR_UNSUPPORTED, "values must be %s for this cache", want == PKV_F32 ? "f32" : "bf16");
+    if (n_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !slots) return fail(PKV_ERR_INVALID, "null values or slots");
+    if (block_table && (!rows || !positions || !kv_lens || num_rows <= 0 || max_blocks <= 0))
+        return fail(PKV_ERR_INVALID, "table upkeep needs rows, positions, kv_lens, num_rows and max_blocks");
+    const int64_t elt = c->kv_dtype == PKV_F32 ? 4 : c->kv_dtype == PKV_BF16 ? 2 : 1;
+    const int64_t layer_elems = static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * pkv::kTile;
+    pkv::WriteParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.slots = slots;
+    p.rows = rows;
+    p.positions = positions;
+    p.table = block_table;
+    p.kv_lens = kv_lens;
+    p.k_pool = static_cast<char*>(c->k_pool) + layer * layer_elems * elt;
+    p.v_pool = static_cast<char*>(c->v_pool) + layer * layer_elems * elt;
+    p.k_scale = c->k_scale ? c->k_scale + static_cast<int64_t>(layer) * c->num_kv_heads : nullptr;
+    p.v_scale = c->v_scale ? c->v_scale + static_cast<int64_t>(layer) * c->num_kv_heads : nullptr;
+    p.n = n_tokens;
+    p.hkv = c->num_kv_heads;
+    p.num_blocks = c->num_blocks;
+    p.num_rows = num_rows;
+    p.max_blocks = max_blocks;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (c->kv_dtype) {
+        case PKV_F32: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_F32>, dim3(n_tokens), dim3(256), 0, s, p); break;
+        case PKV_BF16: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_BF16>, dim3(n_tokens), dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_FP8_E4M3>, dim3(n_tokens), dim3(256), 0, s, p); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+int kv_copy_blocks(const pkv_cache* c, const pkv_copy* copies, int32_t n, void* stream) {
+    int st = pkv::check_cache(c);
+    if (st) return st;
+    if (n < 0 || (n > 0 && !copies)) return fail(PKV_ERR_INVALID, "bad copy list");
+    for (int32_t i = 0; i < n; ++i) {
+        const pkv_copy& cp = copies[i];
+        if (cp.src < 0 || cp.src >= c->num_blocks || cp.dst < 0 || cp.dst >= c->num_blocks || cp.src == cp.dst)
+            return fail(PKV_ERR_INVALID, "copy %d: bad blocks %d -> %d", i, cp.src, cp.dst);
+    }
+    const int64_t elt = c->kv_dtype == PKV_F32 ? 4 : c->kv_dtype == PKV_BF16 ? 2 : 1;
+    pkv::CopyParams p{};
+    p.k_pool = static_cast<char*>(c->k_pool);
+    p.v_pool = static_cast<char*>(c->v_pool);
+    p.block_bytes = static_cast<int64_t>(c->num_kv_heads) * pkv::kTile * elt;
+    p.layer_bytes = p.block_bytes * c->num_blocks;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t base = 0; base < n; base += pkv::kCopyBatch) {
+        const int32_t k = n - base < pkv::kCopyBatch ? n - base : pkv::kCopyBatch;
+        for (int32_t i = 0; i < k; ++i) {
+            p.src[i] = copies[base + i].src;
+            p.dst[i] = copies[base + i].dst;
+        }
+        hipLaunchKernelGGL(pkv::kv_copy_kernel, dim3(k, c->num_layers, 2), dim3(256), 0, s, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_copy_blocks launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
+}  // extern "C"

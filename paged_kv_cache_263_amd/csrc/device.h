@@ -1,0 +1,74 @@
+// Device-side helpers shared by the library's kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kD = PKV_HEAD_DIM;       // head dimension
+constexpr int kBS = PKV_BLOCK_SIZE;    // tokens per block
+constexpr int kTile = kBS * kD;        // elements of one (block, kv head) tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T>
+__device__ __forceinline__ T ld(const void* p) {
+    return *static_cast<const T*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void st(void* p, T v) {
+    *static_cast<T*>(p) = v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four fp8 E4M3 bytes -> four bf16 (exact).  The hardware converts E4M3 to
+// fp32 exactly (checked on all 256 codes); an E4M3 value has at most four
+// significant bits, so the fp32 result's low 16 bits are zero and its high
+// half is the bf16 encoding of the same value.
+__device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    return u32x2_t{(__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u),
+                   (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u)};
+}
+
+// fp32 -> E4M3 code: nearest, ties to even mantissa, |x| >= 448 saturates to
+// +-448, sign kept (so -0 and negative underflow give 0x80).  Written from
+// the format: bias 7, subnormals m/8 * 2^-6, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t e4m3_code_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const float af = __uint_as_float(a);
+    if (!(af < 448.0f)) return sign | 0x7Eu;
+    if (af < 0.015625f) {  // below 2^-6: subnormal codes 0..8, code = rint(|x| * 2^9)
+        return sign | static_cast<uint32_t>(__builtin_rintf(af * 512.0f));
+    }
+    int e = static_cast<int>(a >> 23) - 127;  // -6 .. 8
+    uint32_t keep = (a >> 20) & 7u;
+    const uint32_t rest = a & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1;
+    if (keep == 8) {
+        keep = 0;
+        e += 1;
+    }
+    return sign | (static_cast<uint32_t>(e + 7) << 3) | keep;
+}
+
+}  // namespace pkv

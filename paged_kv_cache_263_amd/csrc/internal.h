@@ -1,0 +1,24 @@
+// Internal helpers shared by the library's translation units (not installed).
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+// Record a message for pkv_last_error() and return the status unchanged.
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Argument checks shared by the device entry points (PKV_OK or an error).
+int check_cache(const pkv_cache* c);
+int check_attn(const pkv_cache* c, const pkv_attn_args* a);
+
+// Tokens per split-K chunk for a decode launch.
+int32_t decode_split_tokens(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len);
+
+// Workspace the decode part of a call needs (bytes; 0 when no row is split).
+size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len);
+
+}  // namespace pkv

@@ -1,0 +1,188 @@
+"""CPU checks of the C ABI: the library loads and exports every function the
+header declares; the host allocator matches the oracle's model bit for bit
+(slots, copies, tables, refcounts, free-list order, statistics, errors)."""
+
+import itertools
+import json
+import os
+import random
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_263_amd as pk
+from oracle import pool as OP
+
+from abi_pool import AbiPool
+from test_oracle_pool import GOLDEN, run_golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pagedkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 25 and "paged_attn_decode" in names and "kv_pool_alloc" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(pk._lib, n)
+        assert n in pk.__all__
+
+
+def test_status_strings():
+    assert pk.pkv_strerror(0) == "ok"
+    assert "blocks" in pk.pkv_strerror(-2)
+    assert pk.pkv_version() >= 1
+
+
+def test_golden_scripts_through_the_abi():
+    data = json.load(open(os.path.join(GOLDEN, "alloc_scripts.json")))
+    for script in data["scripts"]:
+        run_golden(lambda n, order: AbiPool(n, order=order), script)
+
+
+def compare(model, abi):
+    assert abi.free_stack == model.free_stack
+    assert list(abi.ref) == model.ref
+    st_m, st_a = model.stats(), abi.stats()
+    for k in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks", "refcount_sum", "cow_count",
+              "num_seqs", "tokens", "waste_tokens"):
+        assert st_m[k] == st_a[k], k
+    live = sorted(model.seqs)
+    assert live == sorted(abi.live)
+    if live:
+        mb = max(len(model.seq_blocks(s)) for s in live) + 1
+        assert abi.block_table(live, mb) == tuple(map(list, model.block_table(live, mb)))
+
+
+def step_both(model, abi, op, rng_choice):
+    """Apply one op to both; they must return the same thing or the same error."""
+    results = []
+    for side in (model, abi):
+        try:
+            results.append(("ok", op(side)))
+        except OP.PoolError as e:
+            results.append(("err", e.code))
+    assert results[0] == results[1], (results, rng_choice)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_scripts_bit_exact(seed):
+    rng = random.Random(1000 + seed)
+    n = rng.choice([3, 5, 8, 17, 40])
+    order = list(range(n))
+    rng.shuffle(order)
+    model, abi = OP.PoolModel(n, order=order), AbiPool(n, order=order)
+    for i in range(250):
+        live = sorted(model.seqs)
+        kind = rng.choice(["create", "append", "append", "append", "fork", "share", "free", "raw", "bad"])
+        if kind == "create" or not live:
+            op = lambda s: s.seq_create()
+        elif kind == "append":
+            q, k = rng.choice(live), rng.choice([0, 1, 2, 15, 16, 17, 33])
+            op = lambda s, q=q, k=k: s.append(q, k)
+        elif kind == "fork":
+            q = rng.choice(live)
+            op = lambda s, q=q: s.fork(q)
+        elif kind == "share":
+            q = rng.choice(live)
+            k = rng.choice([0, 16, 32, 5]) if rng.random() < 0.5 else (model.seq_len(q) // 16) * 16
+            op = lambda s, q=q, k=k: s.share_prefix(q, k)
+        elif kind == "free":
+            q = rng.choice(live + [max(live) + 1])
+            op = lambda s, q=q: s.seq_free(q)
+        elif kind == "raw":
+            k = rng.choice([1, 2])
+            op = lambda s, k=k: s.free(s.alloc(k))
+        else:
+            q = rng.choice(live)
+            op = lambda s, q=q: s.append(q, -1)
+        step_both(model, abi, op, (i, kind))
+        compare(model, abi)
+
+
+def test_exhaustive_small_scripts_bit_exact():
+    ops = [("create",), ("append", 0, 1), ("append", 0, 16), ("append", 1, 17), ("fork", 0), ("share", 0),
+           ("free", 0)]
+    for depth in range(1, 5):
+        for script in itertools.product(ops, repeat=depth):
+            model, abi = OP.PoolModel(4), AbiPool(4)
+            for op in script:
+                live = sorted(model.seqs)
+                if op[0] == "create":
+                    f = lambda s: s.seq_create()
+                elif not live:
+                    continue
+                elif op[0] == "append":
+                    q = live[op[1] % len(live)]
+                    f = lambda s, q=q, k=op[2]: s.append(q, k)
+                elif op[0] == "fork":
+                    f = lambda s, q=live[0]: s.fork(q)
+                elif op[0] == "share":
+                    q = live[-1]
+                    f = lambda s, q=q, k=(model.seq_len(q) // 16) * 16: s.share_prefix(q, k)
+                else:
+                    f = lambda s, q=live[0]: s.seq_free(q)
+                step_both(model, abi, f, script)
+            compare(model, abi)
+
+
+def test_append_batch_is_all_or_nothing_and_matches_single_appends():
+    order = list(range(12))
+    random.Random(5).shuffle(order)
+    a = pk.kv_pool_create(12, order)
+    b = OP.PoolModel(12, order=order)
+    seqs = [pk.seq_create(a) for _ in range(3)]
+    for _ in range(3):
+        b.seq_create()
+    slots, copies = pk.seq_append_batch(a, seqs, [5, 17, 1])
+    ref = []
+    for s, n in zip(seqs, [5, 17, 1]):
+        ref += b.append(s, n)[0]
+    assert slots == ref and copies == []
+    before = pk.kv_pool_free_list(a)
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.seq_append_batch(a, seqs, [200, 1, 1])
+    assert e.value.code == "OOM" and pk.kv_pool_free_list(a) == before
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.seq_append_batch(a, [seqs[0], seqs[0]], [1, 1])
+    assert e.value.code == "INVALID"
+
+
+def test_error_codes():
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.kv_pool_create(4, block_size=32)
+    assert e.value.code == "UNSUPPORTED"
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.kv_pool_create(3, [0, 1, 1])
+    assert e.value.code == "INVALID"
+    p = pk.kv_pool_create(4)
+    s = pk.seq_create(p)
+    pk.seq_free(p, s)
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.seq_free(p, s)
+    assert e.value.code == "STATE"
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.seq_len(p, 7)
+    assert e.value.code == "INVALID"
+    ids = pk.kv_pool_alloc(p, 2)
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.kv_pool_free(p, [ids[0], ids[0]])
+    assert e.value.code == "STATE" and pk.kv_pool_refcount(p, ids[0]) == 1
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.kv_pool_alloc(p, 3)
+    assert e.value.code == "OOM"
+    t = pk.seq_create(p)
+    pk.seq_append(p, t, 30)
+    with pytest.raises(pk.PagedKVError):
+        pk.block_table_build(p, [t], 1)
