@@ -1,0 +1,286 @@
+"""Paged GQA decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+One step is one decode step of the whole hot path for a batch of sequences
+whose K/V already sit in the paged cache in HBM:
+  1. host allocator: one new token for every sequence (a new block every 16
+     tokens, copy-on-write if the tail block is shared), slots returned;
+  2. one host-to-device copy of the slots and positions;
+  3. cache write: the new tokens' K/V to their slots, device block table and
+     lengths kept up to date in the same kernel;
+  4. paged decode: the split kernel over the blocks of each sequence, then the
+     merge kernel for sequences split over several chunks.
+``value`` is the KV bytes every step attends (sum of lengths x kv heads x 128
+x 2 x element bytes) divided by the measured step time.  The line also
+carries the roofline of the dominant kernel (the decode split kernel, timed
+with HIP events recorded on its stream by the library around it), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Default workload: a Llama-3-8B-shaped decode layer: 64 sequences, lengths
+uniform on 512..8192, 32 query / 8 kv heads, d = 128, bf16, 16-token blocks
+placed by a seeded shuffle in a pool 1.2x the blocks needed.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+WORKLOADS = ("llama8b", "shared_prefix", "fp8_long")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+def build_workload(name: str):
+    import workloads as W
+
+    return {"llama8b": W.llama8b, "shared_prefix": W.shared_prefix, "fp8_long": W.fp8_long}[name]()
+
+
+def describe(w) -> str:
+    return {
+        "llama8b": "Llama-3-8B-shaped paged GQA decode layer: batch 64, 32 q / 8 kv heads, d 128, bf16 K/V/Q, "
+                   "KV lengths uniform 512-8192, 16-token blocks shuffled in a pool 1.2x need",
+        "shared_prefix": "shared-prefix paged decode: 256 seqs sharing a 2000-token prefix (125 blocks) + unique "
+                         "suffix 50-1000, 64 q / 8 kv heads, bf16, one copy-on-write",
+        "fp8_long": "long-context fp8 paged decode: batch 16, KV length 131072, 64 q / 8 kv heads, fp8 E4M3 K/V "
+                    "with per-head fp32 scales, bf16 Q",
+    }[w.name]
+
+
+def setup(w, device):
+    """Fill the paged cache through the library: replay the workload script on
+    the host allocator, write every append's values with the cache-write
+    kernel (and run copy-on-write copies)."""
+    import paged_kv_cache_263_amd as pk
+    import workloads as W
+
+    pool = pk.kv_pool_create(w.num_blocks, w.placement)
+    ks = vs = None
+    if w.kv_dtype == "fp8":
+        ks, vs = w.k_scale.reshape(1, -1), w.v_scale.reshape(1, -1)
+    cache = pk.KVCache(w.kv_dtype, 1, w.num_blocks, w.hkv, device, k_scale=ks, v_scale=vs, zero=False)
+    lens, starts = W.replay_lengths(w)
+    for op in w.script:
+        if op.kind == "create":
+            pk.seq_create(pool)
+        elif op.kind == "append":
+            slots, copies = pk.seq_append(pool, op.seq, op.n)
+            if copies:
+                pk.kv_copy_blocks(cache, copies)
+            k, v = W.append_values(w, op, device, starts[op.op_id], lens[op.seq])
+            pk.kv_cache_write(cache, k, v, torch.tensor(slots, dtype=torch.int32, device=device))
+            del k, v
+        elif op.kind == "share_prefix":
+            pk.seq_share_prefix(pool, op.seq, op.n)
+        elif op.kind == "fork":
+            pk.seq_fork(pool, op.seq)
+    torch.cuda.synchronize()
+    return pool, cache
+
+
+def cpu_baseline(w, device, rows: int):
+    """The oracle as it stands, on a bounded sample: the oracle's pool model
+    replays the script, then for the first ``rows`` batch rows it reads every
+    row's K/V through its own table (fp8: through its own codec) and computes
+    fp64 attention for all query heads.  Reported in the metric's unit: KV
+    bytes of the sampled rows / oracle seconds."""
+    from threadpoolctl import threadpool_info
+
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import fp8 as OF
+    from oracle import pool as OP
+
+    model = OP.PoolModel(w.num_blocks, order=w.placement)
+    store = OP.TokenStore(w.num_blocks, (), np.int64)
+    final, starts = W.replay_lengths(w)
+    ops = {}
+    for op in w.script:
+        if op.kind == "create":
+            model.seq_create()
+        elif op.kind == "append":
+            slots, copies = model.append(op.seq, op.n)
+            for c in copies:
+                store.copy_block(c)
+            store.write(slots, (np.int64(op.op_id) << 32) + np.arange(op.n, dtype=np.int64))
+            ops[op.op_id] = op
+        elif op.kind == "share_prefix":
+            model.share_prefix(op.seq, op.n)
+        elif op.kind == "fork":
+            model.fork(op.seq)
+    # inputs for the sample (generator output, moved to host; not timed)
+    sample = []
+    for row in range(rows):
+        seq = w.batch[row]
+        L = model.seq_len(seq)
+        ids = store.gather(model.seq_blocks(seq), L)
+        op_ids, offs = ids >> 32, ids & 0xFFFFFFFF
+        vals = {}
+        for oid in np.unique(op_ids):
+            op = ops[int(oid)]
+            k, v = W.append_values(w, op, device, starts[op.op_id], final[op.seq])
+            vals[int(oid)] = (k.float().cpu().numpy(), v.float().cpu().numpy())
+        q = W.query_row(w, row, device)[0].float().cpu().numpy()
+        sample.append((seq, L, op_ids, offs, vals, q))
+    t0 = time.perf_counter()
+    kv_bytes = 0
+    for seq, L, op_ids, offs, vals, q in sample:
+        # gather through the oracle's table happened above for the ids; the
+        # value gather, fp8 codec and fp64 attention are timed here
+        K = np.empty((L, w.hkv, w.d))
+        V = np.empty((L, w.hkv, w.d))
+        for oid, (k, v) in vals.items():
+            sel = np.nonzero(op_ids == oid)[0]
+            kk, vv = k[offs[sel]], v[offs[sel]]
+            if w.kv_dtype == "fp8":
+                kk = OF.dequantise(OF.quantise_scaled(kk, w.k_scale[None, :, None]), w.k_scale[None, :, None])
+                vv = OF.dequantise(OF.quantise_scaled(vv, w.v_scale[None, :, None]), w.v_scale[None, :, None])
+            K[sel], V[sel] = kk, vv
+        OA.decode(q, K, V)
+        kv_bytes += L * w.hkv * w.d * 2 * elt_bytes(w)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {len(w.batch)} rows (all {w.hq} query heads, full lengths), "
+                      f"{kv_bytes / 1e9:.3f} GB of KV in {dt:.2f} s; fp64 numpy",
+            "seconds": dt}
+
+
+def elt_bytes(w) -> int:
+    return {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU: the paged decode path has no multi-GPU "
+                                   "mode (no sharding or collectives); run with --gpus 1"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import paged_kv_cache_263_amd as pk
+
+    device = "cuda"
+    torch.cuda.set_device(0)
+    w = build_workload(args.workload)
+    pool, cache = setup(w, device)
+    B = len(w.batch)
+    seqs = list(w.batch)
+    lens = np.array([pk.seq_len(pool, s) for s in seqs], dtype=np.int64)
+    total = args.warmup + args.steps
+    max_blocks = int(math.ceil((lens.max() + total) / 16)) + 1
+    table_h, lens_h = pk.block_table_build(pool, seqs, max_blocks)
+    d_table = table_h.to(device)
+    d_lens = lens_h.to(device)
+    q = __import__("workloads").queries(w, device)
+    out = torch.empty_like(q)
+    g = torch.Generator(device=device).manual_seed(w.seed + 5)
+    k_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
+    v_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
+    d_rows = torch.arange(B, dtype=torch.int32, device=device)
+    h_io = torch.empty((total, 2, B), dtype=torch.int32).pin_memory()  # slots, positions per step
+    d_io = torch.empty((2, B), dtype=torch.int32, device=device)
+    ones = [1] * B
+    # workspace sized for the longest row the run reaches
+    a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.split_tokens, None)
+    ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    for row in ev:
+        for e in row:
+            e.record(stream)  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+
+    kv_bytes_step = []
+    copies_total = 0
+
+    def step(i):
+        nonlocal copies_total
+        slots, copies = pk.seq_append_batch(pool, seqs, ones, out_slots=h_io[i, 0])
+        if copies:
+            pk.kv_copy_blocks(cache, copies)
+            copies_total += len(copies)
+        h_io[i, 1].copy_(torch.from_numpy(lens.astype(np.int32)))  # position of the new token
+        lens[:] += 1
+        d_io.copy_(h_io[i], non_blocking=True)
+        ev[i][0].record(stream)
+        pk.kv_cache_write(cache, k_new[i], v_new[i], d_io[0], rows=d_rows, positions=d_io[1],
+                          block_table=d_table, kv_lens=d_lens)
+        pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, split_tokens=args.split_tokens,
+                             workspace=ws, events=[ev[i][1].cuda_event, ev[i][2].cuda_event, ev[i][3].cuda_event])
+        kv_bytes_step.append(int(lens.sum()) * w.hkv * w.d * 2 * elt_bytes(w))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    timed = range(args.warmup, total)
+    split_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
+    merge_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in timed]
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
+    bytes_timed = kv_bytes_step[args.warmup:]
+    ms_per_step = dt * 1e3 / args.steps
+    value = sum(bytes_timed) / dt / 1e9
+    tokens_per_s = sum(b / (w.hkv * w.d * 2 * elt_bytes(w)) for b in bytes_timed) / dt
+    split_avg_s = float(np.mean(split_ms)) / 1e3
+    achieved = float(np.mean(bytes_timed)) / split_avg_s / 1e9
+
+    result = {
+        "metric": "paged GQA decode: achieved HBM GB/s (KV bytes) + seq-tokens attended/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "f32": "f32"}[w.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": describe(w), "batch": B, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
+                   "block_size": 16, "mean_kv_len": round(float(np.mean(lens)), 1),
+                   "pool_blocks": w.num_blocks, "split_tokens": args.split_tokens or "auto"},
+        "seq_tokens_per_s": round(tokens_per_s, 1),
+        "kernels_us": {"decode_split": round(float(np.mean(split_ms)) * 1e3, 2),
+                       "decode_merge": round(float(np.mean(merge_ms)) * 1e3, 2),
+                       "cache_write": round(float(np.mean(write_ms)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split_kernel (KV bytes of all rows per launch / event-timed duration)"},
+        "copy_on_write_copies": copies_total,
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_sample_rows or {"llama8b": 8, "shared_prefix": 32, "fp8_long": 1}[w.name]
+        result["cpu_baseline"] = cpu_baseline(w, device, rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

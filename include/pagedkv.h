@@ -190,6 +190,11 @@ typedef struct {
     int32_t split_tokens;        /* tokens per split-K chunk, multiple of 16, <= 1024; 0 = auto */
     void* workspace;             /* device scratch for split-K partials */
     size_t workspace_bytes;
+    /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
+     * the call records on its stream: [0] before its first kernel, [1] after
+     * the decode split kernel, [2] after the decode merge kernel (or where it
+     * would be), [3] after the prefill kernel.  The caller owns the events. */
+    void* events[4];
 } pkv_attn_args;
 
 /* Bytes of workspace paged_attn_decode / paged_attn_prefill_chunk need for

@@ -97,3 +97,19 @@ def decode_rows(q, K, V, heads) -> np.ndarray:
         w = np.exp(s - s.max())
         out[n] = (w @ Vj) / w.sum()
     return out
+
+
+def prefill_rows(q, K, V, rows) -> np.ndarray:
+    """Chosen queries of a chunk: q [C, Hq, d] are the last C of the L tokens in
+    K, V [L, Hkv, d]; for each query index i in ``rows`` (attending keys
+    0..L-C+i, as in ``prefill_chunk``) returns [len(rows), Hq, d] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    C, hq, d = q.shape
+    L = np.asarray(K).shape[0]
+    if C > L:
+        raise ValueError("chunk longer than the cached sequence")
+    out = np.empty((len(rows), hq, d), dtype=np.float64)
+    for n, i in enumerate(rows):
+        last = L - C + int(i) + 1
+        out[n] = decode(q[int(i)], np.asarray(K[:last]), np.asarray(V[:last]))
+    return out

@@ -69,7 +69,8 @@ class pkv_attn_args(ctypes.Structure):
                 ("cu_q", ctypes.c_void_p), ("num_decode", ctypes.c_int32),
                 ("max_decode_kv_len", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("total_q", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("events", ctypes.c_void_p * 4)]
 
 
 _i32, _p, _pi32 = ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
@@ -355,6 +356,12 @@ def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, split
           cu_q=None, num_decode=0, max_decode_kv_len=0, max_q_len=0, total_q=0) -> pkv_attn_args:
     if q.dtype not in _QDT:
         raise PagedKVError(-4, f"query dtype {q.dtype}")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or out.shape != q.shape or out.dtype != q.dtype:
+        raise PagedKVError(-1, "q and out must be [rows, heads, 128] of one dtype")
+    if cu_q is None and q.shape[0] != block_table.shape[0]:
+        raise PagedKVError(-1, "decode needs one query row per block-table row")
+    if kv_lens.numel() != block_table.shape[0]:
+        raise PagedKVError(-1, "kv_lens needs one entry per block-table row")
     for t in (q, out, block_table, kv_lens):
         if not t.is_contiguous():
             raise PagedKVError(-1, "tensors must be contiguous")
@@ -399,12 +406,20 @@ def _with_workspace(cache, a, workspace, device):
     return workspace
 
 
+def _set_events(a, events):
+    if events is not None:
+        for i, e in enumerate(events):
+            a.events[i] = e
+
+
 def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, out=None, layer: int = 0,
-                      split_tokens: int = 0, workspace=None, stream=None):
-    """q [rows, Hq, 128] -> out [rows, Hq, 128] (q's dtype)."""
+                      split_tokens: int = 0, workspace=None, stream=None, events=None):
+    """q [rows, Hq, 128] -> out [rows, Hq, 128] (q's dtype).  ``events``: up to
+    four hipEvent_t handles (ints) recorded around the kernels (see the header)."""
     if out is None:
         out = torch.empty_like(q)
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace)
+    _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841 (alive until enqueued)
     _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
     return out
@@ -412,13 +427,14 @@ def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, 
 
 def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_kv_len: int, num_decode: int,
                              max_q_len: int, out=None, layer: int = 0, max_decode_kv_len: int = 0,
-                             split_tokens: int = 0, workspace=None, stream=None):
+                             split_tokens: int = 0, workspace=None, stream=None, events=None):
     """q [total_q, Hq, 128]; rows 0..num_decode-1 are decode rows (cu_q[i] = i)."""
     if out is None:
         out = torch.empty_like(q)
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace, cu_q=cu_q,
               num_decode=num_decode, max_decode_kv_len=max_decode_kv_len, max_q_len=max_q_len,
               total_q=q.shape[0])
+    _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841
     _check(_lib.paged_attn_prefill_chunk(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
     return out
@@ -433,6 +449,12 @@ def kv_cache_write(cache: KVCache, k_new, v_new, slots, layer: int = 0, rows=Non
         if not t.is_contiguous():
             raise PagedKVError(-1, "tensors must be contiguous")
     n = int(slots.numel())
+    want = (n, cache.num_kv_heads, HEAD_DIM)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want or slots.dtype != torch.int32:
+        raise PagedKVError(-1, f"k_new/v_new must be {want} and slots int32 [n]")
+    for t in (rows, positions):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != n):
+            raise PagedKVError(-1, "rows/positions must be int32 [n]")
     num_rows = int(block_table.shape[0]) if block_table is not None else 0
     max_blocks = int(block_table.shape[1]) if block_table is not None else 0
     _check(_lib.kv_cache_write(ctypes.byref(cache.desc), layer, n,

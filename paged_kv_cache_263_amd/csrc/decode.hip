@@ -354,7 +354,11 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
                   hipStream_t stream) {
-    if (rows <= 0) return PKV_OK;
+    if (rows <= 0) {
+        for (int i = 0; i < 3; ++i)
+            if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
+        return PKV_OK;
+    }
     const int32_t st_tokens = decode_split_tokens(c, a, rows, max_kv_len);
     const int32_t splits = (max_kv_len + st_tokens - 1) / st_tokens;
     const size_t need = decode_workspace_bytes(c, a, rows, max_kv_len);
@@ -387,6 +391,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.max_splits = splits;
     p.scale_log2 = kLog2e / sqrtf(static_cast<float>(kD));
 
+    auto mark = [&](int i) {
+        if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
+    };
+    mark(0);
     switch (c->kv_dtype) {
         case PKV_F32:
             hipLaunchKernelGGL(decode_split_kernel<PKV_F32>, dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, p);
@@ -398,6 +406,7 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
             hipLaunchKernelGGL(decode_split_kernel<PKV_FP8_E4M3>, dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, p);
             break;
     }
+    mark(1);
     if (splits > 1) {
         const int64_t mgrid = static_cast<int64_t>(rows) * a->num_q_heads;
         if (a->q_dtype == PKV_F32)
@@ -405,6 +414,7 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
         else
             hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, dim3(static_cast<unsigned>(mgrid)), dim3(128), 0, stream, p);
     }
+    mark(2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return PKV_OK;

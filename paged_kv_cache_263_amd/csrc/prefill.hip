@@ -56,7 +56,7 @@ struct PrefillParams {
     const int32_t* table;   // [num_seqs][max_blocks]
     const int32_t* kv_lens; // [num_seqs]
     const int32_t* cu_q;    // [num_seqs + 1]
-    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles;
+    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q;
     float scale_log2;
 };
 
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const int qbeg = p.cu_q[row];
     const int C = p.cu_q[row + 1] - qbeg;
     const int j0 = qt * kQTile;
-    if (j0 >= C) return;
+    if (j0 >= C || qbeg < 0 || qbeg + C > p.total_q) return;  // (a malformed cu_q writes nothing)
     const int L = p.kv_lens[row];
     const bool row_ok = C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS;
     const int P = L - C;
@@ -345,7 +345,8 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     if (!a->cu_q) return fail(PKV_ERR_INVALID, "prefill needs cu_q");
     if (a->num_decode < 0 || a->num_decode > a->num_seqs) return fail(PKV_ERR_INVALID, "bad num_decode %d", a->num_decode);
     const int32_t n_pre = a->num_seqs - a->num_decode;
-    if (n_pre > 0 && a->max_q_len <= 0) return fail(PKV_ERR_INVALID, "max_q_len must be positive");
+    if (n_pre > 0 && (a->max_q_len <= 0 || a->total_q < a->num_decode + n_pre))
+        return fail(PKV_ERR_INVALID, "max_q_len must be positive and total_q must cover every row");
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     // decode rows: queries 0..num_decode-1, one per row
@@ -354,7 +355,10 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     st = pkv::launch_decode(c, a, a->num_decode, dec_len, a->q, a->out, a->block_table, a->kv_lens,
                             a->workspace, a->workspace_bytes, s);
     if (st) return st;
-    if (n_pre == 0) return PKV_OK;
+    if (n_pre == 0) {
+        if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
+        return PKV_OK;
+    }
 
     const int32_t group = a->num_q_heads / c->num_kv_heads;
     const int32_t nt = (group + 3) / 4;
@@ -381,11 +385,13 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.max_blocks = a->max_blocks;
     p.max_kv_len = a->max_kv_len;
     p.q_tiles = q_tiles;
+    p.total_q = a->total_q;
     p.scale_log2 = pkv::kLog2e / sqrtf(static_cast<float>(pkv::kD));
     if (c->kv_dtype == PKV_BF16)
         pkv::launch_prefill_kv<PKV_BF16>(nt, dim3(static_cast<unsigned>(grid)), s, p);
     else
         pkv::launch_prefill_kv<PKV_FP8_E4M3>(nt, dim3(static_cast<unsigned>(grid)), s, p);
+    if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return PKV_OK;

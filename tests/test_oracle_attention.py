@@ -133,3 +133,12 @@ def test_rejects():
         A.decode(np.zeros((4, 8)), np.zeros((0, 2, 8)), np.zeros((0, 2, 8)))
     with pytest.raises(ValueError):
         A.decode(np.zeros((3, 8)), np.zeros((2, 2, 8)), np.zeros((2, 2, 8)))
+
+
+def test_prefill_rows_are_chunk_rows():
+    L, C, hq, hkv, d = 45, 12, 8, 2, 16
+    q = rnd((C, hq, d), 30, 2.0)
+    K, V = rnd((L, hkv, d), 31), rnd((L, hkv, d), 32)
+    full = A.prefill_chunk(q, K, V)
+    rows = [0, 5, 11]
+    np.testing.assert_allclose(A.prefill_rows(q, K, V, rows), full[rows], rtol=0, atol=1e-13)

@@ -224,6 +224,51 @@ def fp8_long(seed: int = 5, variant: str = "plain", batch: int = 16, length: int
                     k_scale=k_scale, v_scale=v_scale, own_ranges=own)
 
 
+def custom(lens, hq: int, hkv: int, kv_dtype: str = "bf16", seed: int = 11, variant: str = "plain",
+           pool_factor: float = 1.2, name: str = "custom") -> Workload:
+    """Decode rows of the given lengths (edge cases, small parity cases)."""
+    script, own = [], {}
+    for s, L in enumerate(lens):
+        script.append(Op("create"))
+        script.append(Op("append", s, int(L), op_id=s))
+        own[s] = [(0, int(L))]
+    nb = max(1, _pool_size(sum(_blocks(int(L)) for L in lens), pool_factor))
+    w = Workload(name, hq, hkv, 128, "f32" if kv_dtype == "f32" else ("bf16" if kv_dtype == "bf16" else "bf16"),
+                 "f32" if kv_dtype == "f32" else "bf16", nb, placement(nb, seed), script,
+                 list(range(len(lens))), [1] * len(lens), seed, variant, own_ranges=own)
+    return scaled_fp8(w) if kv_dtype == "fp8" else w
+
+
+def chunks(rows, hq: int = 64, hkv: int = 8, kv_dtype: str = "bf16", seed: int = 12, n_decode: int = 0,
+           decode_len: int = 300, variant: str = "plain") -> Workload:
+    """Decode rows first, then chunk rows given as (context, chunk) pairs: the
+    context tokens and the chunk's own tokens are written, and the chunk's
+    queries are the new ones."""
+    script, own, q_lens = [], {}, []
+    op = 0
+    s = 0
+    for _ in range(n_decode):
+        script.append(Op("create"))
+        script.append(Op("append", s, decode_len, op_id=op)); op += 1
+        own[s] = [(0, decode_len)]
+        q_lens.append(1)
+        s += 1
+    logical = n_decode * _blocks(decode_len)
+    for ctx, c in rows:
+        script.append(Op("create"))
+        if ctx > 0:
+            script.append(Op("append", s, ctx, op_id=op)); op += 1
+        script.append(Op("append", s, c, op_id=op)); op += 1
+        own[s] = [(0, ctx + c)]
+        q_lens.append(c)
+        logical += _blocks(ctx + c)
+        s += 1
+    nb = _pool_size(logical)
+    w = Workload("chunks", hq, hkv, 128, "bf16", "bf16", nb, placement(nb, seed), script,
+                 list(range(s)), q_lens, seed, variant, own_ranges=own)
+    return scaled_fp8(w) if kv_dtype == "fp8" else w
+
+
 def scaled_fp8(w: Workload) -> Workload:
     """Give a bf16 workload fp8 storage with seeded per-head scales."""
     rng = np.random.default_rng(w.seed + 77)
