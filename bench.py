@@ -35,7 +35,8 @@ import numpy as np
 import torch
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
-WORKLOADS = ("llama8b", "shared_prefix", "fp8_long")
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "chunked")
 
 
 def parse():
@@ -45,14 +46,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--context", type=int, default=16384, help="chunked: cached context before the chunk")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"), help="chunked: cache dtype")
+    ap.add_argument("--placement", default="shuffled", choices=("shuffled", "identity"),
+                    help="physical block order: the workload's seeded shuffle, or identity (a contiguous control)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a dispatch of known size that "
+                         "scales hardware byte counters)")
     return ap.parse_args()
 
 
-def build_workload(name: str):
+def build_workload(name: str, args=None):
     import workloads as W
 
+    if name == "chunked":
+        w = W.chunked(context=args.context)
+        return W.scaled_fp8(w) if args.kv == "fp8" else w
     return {"llama8b": W.llama8b, "shared_prefix": W.shared_prefix, "fp8_long": W.fp8_long}[name]()
 
 
@@ -64,7 +75,74 @@ def describe(w) -> str:
                          "suffix 50-1000, 64 q / 8 kv heads, bf16, one copy-on-write",
         "fp8_long": "long-context fp8 paged decode: batch 16, KV length 131072, 64 q / 8 kv heads, fp8 E4M3 K/V "
                     "with per-head fp32 scales, bf16 Q",
+        "chunked": "chunked prefill: one 1024-query causal chunk over cached context, batched with 32 decode "
+                   "rows of 4096 tokens, 64 q / 8 kv heads, d 128",
     }[w.name]
+
+
+def run_chunked(args, w, device):
+    """Times paged_attn_prefill_chunk on a fixed cache state (chunk K/V already
+    written): the prefill kernel (MFMA-bound) and the decode rows' kernels."""
+    import paged_kv_cache_263_amd as pk
+
+    pool, cache = setup(w, device)
+    lens = [pk.seq_len(pool, s) for s in w.batch]
+    mb = max(-(-L // 16) for L in lens)
+    table_h, lens_h = pk.block_table_build(pool, w.batch, mb)
+    table, klens = table_h.to(device), lens_h.to(device)
+    q = __import__("workloads").queries(w, device)
+    nd = sum(1 for n in w.q_lens if n == 1)
+    cu = [0]
+    for n in w.q_lens:
+        cu.append(cu[-1] + n)
+    cu_q = torch.tensor(cu, dtype=torch.int32, device=device)
+    out = torch.empty_like(q)
+    total = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
+    stream = torch.cuda.current_stream()
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    mdl = max(lens[:nd])
+    a = pk._args(cache, q, out, table, klens, max(lens), 0, args.split_tokens, None, cu_q=cu_q, num_decode=nd,
+                 max_decode_kv_len=mdl, max_q_len=max(w.q_lens), total_q=q.shape[0])
+    ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
+    torch.cuda.synchronize()
+
+    def step(i):
+        pk.paged_attn_prefill_chunk(cache, q, cu_q, table, klens, max(lens), nd, max(w.q_lens), out=out,
+                                    max_decode_kv_len=mdl, split_tokens=args.split_tokens, workspace=ws,
+                                    events=[e.cuda_event for e in ev[i]])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    timed = range(args.warmup, total)
+    dec_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in timed]))
+    pre_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in timed]))
+    C = max(w.q_lens)
+    P = lens[-1] - C
+    flops = 4.0 * w.d * w.hq * (C * P + C * (C + 1) / 2)
+    dec_bytes = sum(lens[:nd]) * w.hkv * w.d * 2 * elt_bytes(w)
+    tflops = flops / (pre_ms / 1e3) / 1e12
+    return {
+        "metric": "chunked prefill + decode rows: prefill TFLOP/s (causal algorithmic flops)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 kv / bf16 q",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "context": P, "chunk": C, "decode_rows": nd},
+        "kernels_us": {"decode_part": round(dec_ms * 1e3, 2), "prefill": round(pre_ms * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel"},
+        "decode_part_gbs": round(dec_bytes / (dec_ms / 1e3) / 1e9, 1),
+    }
 
 
 def setup(w, device):
@@ -183,7 +261,19 @@ def main():
 
     device = "cuda"
     torch.cuda.set_device(0)
-    w = build_workload(args.workload)
+    if args.workload == "chunked":
+        print(json.dumps(run_chunked(args, build_workload("chunked", args), device)), flush=True)
+        return
+    if args.calibrate_copy_mib:
+        src = torch.ones(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    w = build_workload(args.workload, args)
+    if args.placement == "identity":
+        w.placement = np.arange(w.num_blocks, dtype=np.int32)
     pool, cache = setup(w, device)
     B = len(w.batch)
     seqs = list(w.batch)
@@ -235,8 +325,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    host = 0.0
     for i in range(args.warmup, total):
+        h0 = time.perf_counter()
         step(i)
+        host += time.perf_counter() - h0
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
@@ -266,7 +359,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w), "batch": B, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "block_size": 16, "mean_kv_len": round(float(np.mean(lens)), 1),
-                   "pool_blocks": w.num_blocks, "split_tokens": args.split_tokens or "auto"},
+                   "pool_blocks": w.num_blocks, "split_tokens": args.split_tokens or "auto",
+                   "placement": args.placement},
         "seq_tokens_per_s": round(tokens_per_s, 1),
         "kernels_us": {"decode_split": round(float(np.mean(split_ms)) * 1e3, 2),
                        "decode_merge": round(float(np.mean(merge_ms)) * 1e3, 2),
@@ -275,6 +369,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_split_kernel (KV bytes of all rows per launch / event-timed duration)"},
         "copy_on_write_copies": copies_total,
+        "host_us_per_step": round(host * 1e6 / args.steps, 1),
     }
     if not args.no_cpu_baseline:
         rows = args.cpu_sample_rows or {"llama8b": 8, "shared_prefix": 32, "fp8_long": 1}[w.name]

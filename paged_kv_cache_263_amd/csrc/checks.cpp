@@ -50,11 +50,12 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
 
 int32_t decode_split_tokens(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len) {
     if (a->split_tokens) return a->split_tokens;
-    // Enough work items to fill 256 CUs several times over, without making the
-    // partial results a visible share of the KV bytes.
+    // The largest chunk that still gives ~8K work items (32 per CU): long rows
+    // get long chunks (fewer partial results to write and merge), short
+    // batches get short ones (enough work items to fill 256 CUs).
     const int64_t pairs = static_cast<int64_t>(rows) * c->num_kv_heads;
-    for (int32_t st : {512, 256, 128}) {
-        if (pairs * ((max_kv_len + st - 1) / st) >= 2048) return st;
+    for (int32_t st : {1024, 512, 256, 128}) {
+        if (pairs * ((max_kv_len + st - 1) / st) >= 8192) return st;
     }
     return 64;
 }

@@ -30,6 +30,7 @@
 // chunk boundaries, fixed merge order), so a permutation of the physical
 // blocks changes no bit of the output.
 #include <cmath>
+#include <cstdlib>
 
 #include "device.h"
 #include "internal.h"
@@ -223,7 +224,7 @@ struct Online {
     }
 };
 
-template <int KV>
+template <int KV, int NBUF>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
@@ -279,25 +280,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
     Tile<KV>::load_q(q, static_cast<const char*>(p.q) + qrow * kD * kQBytes, head_ok, g);
 
     Online o;
-    Tile<KV> ta, tb2;
-    {
-        const int64_t b = __builtin_amdgcn_readlane(tb, 0);
-        ta.load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
+    // Ring of NBUF register tiles: while block j is computed, blocks
+    // j+1 .. j+NBUF-1 are in flight.
+    Tile<KV> t[NBUF];
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) {
+        if (u < nblk) {
+            const int64_t b = __builtin_amdgcn_readlane(tb, u);
+            t[u].load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
+        }
     }
-    // Two tiles in flight: the next block's loads are issued before the
-    // current block is computed.
-    for (int j = 0; j < nblk; j += 2) {
-        if (j + 1 < nblk) {
-            const int64_t b = __builtin_amdgcn_readlane(tb, j + 1);
-            tb2.load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
+    for (int j0 = 0; j0 < nblk; j0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            const int j = j0 + u;
+            if (j >= nblk) break;
+            const int jn = j + NBUF - 1;
+            if (jn < nblk) {
+                const int64_t b = __builtin_amdgcn_readlane(tb, jn);
+                t[(u + NBUF - 1) % NBUF].load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
+            }
+            o.step<KV>(t[u], q, scale, t0 + j * kBS + 4 * g, t1);
         }
-        o.step<KV>(ta, q, scale, t0 + j * kBS + 4 * g, t1);
-        if (j + 1 >= nblk) break;
-        if (j + 2 < nblk) {
-            const int64_t b = __builtin_amdgcn_readlane(tb, j + 2);
-            ta.load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
-        }
-        o.step<KV>(tb2, q, scale, t0 + (j + 1) * kBS + 4 * g, t1);
     }
 
     float l = o.l;
@@ -319,9 +323,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 }
 
 // Merge the chunks of one (row, query head): out = sum_i acc_i 2^(m_i - M) /
-// sum_i l_i 2^(m_i - M), M = max_i m_i, in chunk order.
+// sum_i l_i 2^(m_i - M), M = max_i m_i.  The weights are computed once into
+// LDS; each lane (one per d) then sums the chunks in chunk order.
+constexpr int kMaxSplits = 4096;
 template <int QT>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p) {
+    __shared__ float wsh[kMaxSplits];
+    __shared__ float red[2];
     const int64_t qrow = blockIdx.x;
     const int row = static_cast<int>(qrow / p.hq);
     const int d = threadIdx.x;
@@ -330,21 +338,46 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
     const int nsplit = row_ok ? (L + p.split_tokens - 1) / p.split_tokens : 1;
     if (nsplit <= 1) return;
     const float* ml = p.ws_ml + 2 * qrow * p.max_splits;
-    const float* acc = p.ws_acc + qrow * p.max_splits * kD + d;
     float mx = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) mx = fmaxf(mx, ml[2 * i]);
-    float num = 0.f, den = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * i] - mx);
-        num += acc[static_cast<int64_t>(i) * kD] * w;
-        den += ml[2 * i + 1] * w;
+    for (int i = d; i < nsplit; i += 128) mx = fmaxf(mx, ml[2 * i]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if ((d & 63) == 0) red[d >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(red[0], red[1]);
+    for (int i = d; i < nsplit; i += 128) wsh[i] = __builtin_amdgcn_exp2f(ml[2 * i] - mx);
+    __syncthreads();
+    // denominator in chunk order (every lane computes the same sum)
+    float den = 0.f;
+    for (int i = 0; i < nsplit; ++i) den += ml[2 * i + 1] * wsh[i];
+    const float* acc = p.ws_acc + qrow * p.max_splits * kD + d;
+    float num = 0.f;
+    int i = 0;
+    for (; i + 4 <= nsplit; i += 4) {
+        const float a0 = acc[static_cast<int64_t>(i) * kD], a1 = acc[static_cast<int64_t>(i + 1) * kD];
+        const float a2 = acc[static_cast<int64_t>(i + 2) * kD], a3 = acc[static_cast<int64_t>(i + 3) * kD];
+        num += a0 * wsh[i];
+        num += a1 * wsh[i + 1];
+        num += a2 * wsh[i + 2];
+        num += a3 * wsh[i + 3];
     }
+    for (; i < nsplit; ++i) num += acc[static_cast<int64_t>(i) * kD] * wsh[i];
     const float o = num / den;
     if constexpr (QT == PKV_F32) {
         static_cast<float*>(p.out)[qrow * kD + d] = o;
     } else {
         static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
     }
+}
+
+// Blocks in flight per wavefront (2..4).  PKV_DECODE_DEPTH overrides the
+// default for tuning runs.
+int decode_pipeline_depth() {
+    static const int depth = [] {
+        const char* e = std::getenv("PKV_DECODE_DEPTH");
+        const int v = e ? std::atoi(e) : 3;
+        return v < 2 ? 2 : (v > 4 ? 4 : v);
+    }();
+    return depth;
 }
 
 }  // namespace
@@ -364,6 +397,7 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     const size_t need = decode_workspace_bytes(c, a, rows, max_kv_len);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(PKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? ws_bytes : 0);
+    if (splits > kMaxSplits) return fail(PKV_ERR_INVALID, "more than %d key chunks per row", kMaxSplits);
     const int64_t grid = static_cast<int64_t>(rows) * splits * c->num_kv_heads;
     if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "decode launch too large");
 
@@ -395,15 +429,21 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
         if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
     };
     mark(0);
+    const dim3 g1(static_cast<unsigned>(grid));
+    const int depth = decode_pipeline_depth();
     switch (c->kv_dtype) {
         case PKV_F32:
-            hipLaunchKernelGGL(decode_split_kernel<PKV_F32>, dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_split_kernel<PKV_F32, 2>), g1, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
-            hipLaunchKernelGGL(decode_split_kernel<PKV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, p);
+            if (depth <= 2) hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 2>), g1, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 3>), g1, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 4>), g1, dim3(64), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL(decode_split_kernel<PKV_FP8_E4M3>, dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, p);
+            if (depth <= 2) hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 2>), g1, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 3>), g1, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 4>), g1, dim3(64), 0, stream, p);
             break;
     }
     mark(1);
