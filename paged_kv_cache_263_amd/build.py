@@ -4,8 +4,8 @@
 
 Every source is compiled with hipcc for gfx950 only.  Packed fp32 arithmetic
 is switched off for device code (ordinary fp32 code is compiled to scalar fp32
-instructions), and fp32 division is the correctly rounded one, which the fp8
-quantiser relies on.
+instructions), fp32 division is the correctly rounded one, which the fp8
+quantiser relies on, and matrix-core accumulators are kept in VGPRs.
 """
 
 from __future__ import annotations
@@ -31,6 +31,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # keep matrix-core accumulators in VGPRs, so the softmax rescale of the
+    # accumulators needs no AGPR<->VGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

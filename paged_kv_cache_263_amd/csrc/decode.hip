@@ -101,6 +101,14 @@ struct Tile<PKV_BF16> {
 #pragma unroll
         for (int n = 0; n < 8; ++n) v[n] = ld<u32x2_t>(vt + (16 * n + r) * kBS + 4 * g);
     }
+    // Zero this lane's V elements of tokens 4g + i with keep[i] false (the
+    // unwritten tail of a block may hold any bits, and 0 * NaN is NaN).
+    __device__ __forceinline__ void mask_v(const bool keep[4]) {
+        const uint32_t lo = (keep[0] ? 0xFFFFu : 0u) | (keep[1] ? 0xFFFF0000u : 0u);
+        const uint32_t hi = (keep[2] ? 0xFFFFu : 0u) | (keep[3] ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) v[n] = u32x2_t{v[n][0] & lo, v[n][1] & hi};
+    }
     __device__ __forceinline__ f32x4_t scores(const Q& q) const {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -134,6 +142,12 @@ struct Tile<PKV_FP8_E4M3> {
         for (int ks = 0; ks < 4; ++ks) k[ks] = ld<u32x2_t>(kt + r * kD + 32 * ks + 8 * g);
 #pragma unroll
         for (int n = 0; n < 8; ++n) v[n] = ld<uint32_t>(vt + (16 * n + r) * kBS + 4 * g);
+    }
+    __device__ __forceinline__ void mask_v(const bool keep[4]) {
+        const uint32_t m = (keep[0] ? 0xFFu : 0u) | (keep[1] ? 0xFF00u : 0u) | (keep[2] ? 0xFF0000u : 0u) |
+                           (keep[3] ? 0xFF000000u : 0u);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) v[n] &= m;
     }
     __device__ __forceinline__ f32x4_t scores(const Q& q) const {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -175,6 +189,12 @@ struct Tile<PKV_F32> {
 #pragma unroll
         for (int n = 0; n < 8; ++n) v[n] = ld<f32x4_t>(vt + (16 * n + r) * kBS + 4 * g);
     }
+    __device__ __forceinline__ void mask_v(const bool keep[4]) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[n][i] = keep[i] ? v[n][i] : 0.f;
+    }
     __device__ __forceinline__ f32x4_t scores(const Q& q) const {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -191,8 +211,18 @@ struct Tile<PKV_F32> {
     }
 };
 
-// Online-softmax state of the lanes of one head (i % 16): running max m (log2
-// units), this lane's partial normaliser l, and the output accumulators.
+// Online-softmax state of the lanes of one head (i % 16): reference max m
+// (log2 units), this lane's partial normaliser l, and the output accumulators.
+//
+// Rescaling is lazy: p = 2^(s - m) is computed against the current reference
+// m, and only when some lane sees a score above m + kLazy does the wave take
+// the cross-lane max and rescale l and the accumulators to the new reference.
+// So every p is at most 2^kLazy (exact in fp32, and split exactly into bf16
+// high and low parts as before), the final result acc / l is unchanged, and
+// the rescale - 32 accumulator multiplies plus two lane shuffles - runs only
+// in the few blocks where the maximum jumps.
+constexpr float kLazy = 8.0f;
+
 struct Online {
     float m = -INFINITY;
     float l = 0.f;
@@ -201,25 +231,37 @@ struct Online {
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // One block: tok = first token of this lane's four (4 g + i); tokens at
+    // or past t1 are masked (score -inf, V zeroed).  blk_end: one past the
+    // block's last token (uniform).
     template <int KV>
-    __device__ __forceinline__ void step(const Tile<KV>& t, const typename Tile<KV>::Q& q, float scale, int tok,
-                                         int t1) {
+    __device__ __forceinline__ void step(Tile<KV>& t, const typename Tile<KV>::Q& q, float scale, int tok, int t1,
+                                         int blk_end) {
+        if (blk_end > t1) {  // partial (or padding) block: uniform branch, no loads inside
+            bool keep[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) keep[i] = tok + i < t1;
+            t.mask_v(keep);
+        }
         const f32x4_t s = t.scores(q);
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (tok + i < t1) ? s[i] * scale : -INFINITY;
         float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mn = fmaxf(m, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        if (__any(mb > m + kLazy)) {  // rare: a new maximum for some head
+            mb = fmaxf(mb, __shfl_xor(mb, 16));
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = fmaxf(m, mb);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+            m = mn;
+        }
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - mn);
-        l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m = mn;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m);
+        l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         t.accumulate(acc, pr);
     }
 };
@@ -281,26 +323,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
 
     Online o;
     // Ring of NBUF register tiles: while block j is computed, blocks
-    // j+1 .. j+NBUF-1 are in flight.
+    // j+1 .. j+NBUF-1 are in flight.  The trip count is padded to a multiple
+    // of NBUF and every load is unconditional (block index clamped to the
+    // last block, a cache hit), so no branch sits between a load and its use
+    // and the compiler's wait counts let the prefetched loads stay in flight.
+    // Padding steps are fully masked and change nothing.
+    const int niter = (nblk + NBUF - 1) / NBUF * NBUF;
+    auto tile_off = [&](int j) -> int64_t {
+        return static_cast<int64_t>(__builtin_amdgcn_readlane(tb, min(j, nblk - 1))) * blk_stride;
+    };
     Tile<KV> t[NBUF];
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) {
-        if (u < nblk) {
-            const int64_t b = __builtin_amdgcn_readlane(tb, u);
-            t[u].load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
-        }
+        const int64_t b = tile_off(u);
+        t[u].load(kpool + b, vpool + b, r, g);
     }
-    for (int j0 = 0; j0 < nblk; j0 += NBUF) {
+    for (int j0 = 0; j0 < niter; j0 += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
             const int j = j0 + u;
-            if (j >= nblk) break;
-            const int jn = j + NBUF - 1;
-            if (jn < nblk) {
-                const int64_t b = __builtin_amdgcn_readlane(tb, jn);
-                t[(u + NBUF - 1) % NBUF].load(kpool + b * blk_stride, vpool + b * blk_stride, r, g);
-            }
-            o.step<KV>(t[u], q, scale, t0 + j * kBS + 4 * g, t1);
+            const int64_t b = tile_off(j + NBUF - 1);
+            t[(u + NBUF - 1) % NBUF].load(kpool + b, vpool + b, r, g);
+            o.step<KV>(t[u], q, scale, t0 + j * kBS + 4 * g, t1, t0 + (j + 1) * kBS);
         }
     }
 

@@ -19,7 +19,8 @@
 // iteration.  Each wave then computes, per head tile (16 tokens of one head):
 //   S^T[64 keys x 16 tokens] = K . Q^T           (16 x mfma 16x16x32 bf16)
 //   O^T[128 x 16 tokens]    += V^T . P^T         (8 d-tiles x 2 key halves, P as bf16 hi + lo)
-// with the running max / normaliser of the decode kernel and the causal mask
+// with the running max / normaliser of the decode kernel (rescaled lazily,
+// only when a score passes the reference max by 2^8) and the causal mask
 // applied only where a key can pass a query's position.  For P.V the 32 keys
 // of one instruction are taken in the order the score tiles leave them in the
 // lanes (keys 4g..4g+3 of two consecutive blocks), and V is read in the same
@@ -45,6 +46,7 @@ constexpr int kKStride = kD + 8;       // padded K row (elements)
 constexpr int kVStride = kBS + 4;      // padded V^T row (elements)
 constexpr int kKStage = 4 * kBS * kKStride;   // elements of one K stage
 constexpr int kVStage = 4 * kD * kVStride;    // elements of one V stage
+constexpr float kLazy = 8.0f;                 // rescale threshold (log2 units)
 
 struct PrefillParams {
     const void* q;          // [total_q][hq][128] bf16
@@ -80,7 +82,10 @@ __device__ __forceinline__ void split_p8(const float p[8], bf16x8_t& hi, bf16x8_
 template <int KV>
 struct Stage {
     u32x4_t k[4], v[4];  // bf16 values (fp8 converted on load)
-    __device__ __forceinline__ void load(const void* kp, const void* vp, const int64_t blk[4], int t) {
+    // valid[b]: tokens of block b at or past it are unwritten (only the row's
+    // last block is partial); their V is zeroed, since 0 * NaN is NaN.
+    __device__ __forceinline__ void load(const void* kp, const void* vp, const int64_t blk[4], const int valid[4],
+                                         int t) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if (blk[b] < 0) {
@@ -102,6 +107,14 @@ struct Stage {
                 const u32x2_t v0 = fp8x4_to_bf16x4(vv[0]), v1 = fp8x4_to_bf16x4(vv[1]);
                 k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
                 v[b] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+            }
+            if (valid[b] < kBS) {  // V^T chunk: tokens (t & 1) * 8 .. +7 of d row t / 2
+                const int tok0 = (t & 1) * 8;
+                uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (tok0 + e >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
             }
         }
     }
@@ -189,7 +202,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const void* vp = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(koff) * (KV == PKV_BF16 ? 2 : 1);
 
     bool bad = false;
-    auto block_offsets = [&](int it, int64_t blk[4]) {
+    auto block_offsets = [&](int it, int64_t blk[4], int valid[4]) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int lb = it * 4 + b;
@@ -200,14 +213,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
                 id = -1;
             }
             blk[b] = id < 0 ? -1 : static_cast<int64_t>(id) * blk_stride;
+            valid[b] = min(kBS, max(0, L - lb * kBS));
         }
     };
 
     Stage<KV> sreg;
     if (n_iter > 0) {
         int64_t blk[4];
-        block_offsets(0, blk);
-        sreg.load(kp, vp, blk, t);
+        int valid[4];
+        block_offsets(0, blk, valid);
+        sreg.load(kp, vp, blk, valid, t);
         sreg.store(ks[0], vs[0], t);
     }
     __syncthreads();
@@ -216,8 +231,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         const int cur = it & 1;
         if (it + 1 < n_iter) {
             int64_t blk[4];
-            block_offsets(it + 1, blk);
-            sreg.load(kp, vp, blk, t);
+            int valid[4];
+            block_offsets(it + 1, blk, valid);
+            sreg.load(kp, vp, blk, valid, t);
         }
         const uint16_t* kc = ks[cur];
         const uint16_t* vc = vs[cur];
@@ -255,21 +271,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
             float mb = x[0];
 #pragma unroll
             for (int i = 1; i < 16; ++i) mb = fmaxf(mb, x[i]);
-            mb = fmaxf(mb, __shfl_xor(mb, 16));
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float mn = fmaxf(m[nt], mb);
-            const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
+            // lazy rescale (as in the decode kernel): only when some score
+            // passes the reference max by more than kLazy
+            if (__any(mb > m[nt] + kLazy)) {
+                mb = fmaxf(mb, __shfl_xor(mb, 16));
+                mb = fmaxf(mb, __shfl_xor(mb, 32));
+                const float mn = fmaxf(m[nt], mb);
+                const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
+                l[nt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[nt][i] *= alpha;
+                m[nt] = mn;
+            }
             float pr[16];
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                pr[i] = __builtin_amdgcn_exp2f(x[i] - mn);
+                pr[i] = __builtin_amdgcn_exp2f(x[i] - m[nt]);
                 sum += pr[i];
             }
-            l[nt] = l[nt] * alpha + sum;
-            m[nt] = mn;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[nt][i] *= alpha;
+            l[nt] += sum;
             // k-step h covers blocks 2h, 2h+1: this lane's 8 keys are
             // (block 2h: 4g..4g+3, block 2h+1: 4g..4g+3)
 #pragma unroll

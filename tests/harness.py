@@ -29,7 +29,7 @@ def blocks(n: int) -> int:
 
 
 class HipSide:
-    def __init__(self, w: W.Workload, device="cuda", placement=None, layer=0, num_layers=1):
+    def __init__(self, w: W.Workload, device="cuda", placement=None, layer=0, num_layers=1, fill_byte=None):
         import paged_kv_cache_263_amd as pk
 
         self.pk = pk
@@ -43,6 +43,9 @@ class HipSide:
             ks = np.tile(w.k_scale, (num_layers, 1))
             vs = np.tile(w.v_scale, (num_layers, 1))
         self.cache = pk.KVCache(w.kv_dtype, num_layers, w.num_blocks, w.hkv, device, k_scale=ks, v_scale=vs)
+        if fill_byte is not None:  # unwritten slots hold this byte pattern (0xFF: NaN in every dtype)
+            self.cache.k_pool.view(torch.uint8).fill_(fill_byte)
+            self.cache.v_pool.view(torch.uint8).fill_(fill_byte)
         lens, starts = W.replay_lengths(w)
         self.n_copies = 0
         for op in w.script:

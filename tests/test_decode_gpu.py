@@ -216,3 +216,11 @@ def test_second_layer():
     w = W.custom([33, 600], 8, 2, "bf16", seed=81, variant="peaked")
     hip = HipSide(w, layer=1, num_layers=2)
     check_decode(w, hip=hip)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+def test_unwritten_slots_hold_nan(kv):
+    """Slots past a row's length (the tail of its last block) and unused pool
+    blocks hold NaN bit patterns: masked tokens must not reach the output."""
+    w = W.custom([1, 17, 300, 513, 1000], 8, 2, kv, seed=91, variant="peaked")
+    check_decode(w, hip=HipSide(w, fill_byte=0xFF))

@@ -82,3 +82,9 @@ def test_prefill_is_deterministic_and_placement_invariant():
     c = HipSide(w).prefill()
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_unwritten_slots_hold_nan(kv):
+    w = W.chunks([(5, 16), (100, 33), (0, 1)], hq=8, hkv=2, kv_dtype=kv, n_decode=2, variant="peaked", seed=23)
+    check_prefill(w, hip=HipSide(w, fill_byte=0xFF))
