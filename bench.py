@@ -9,11 +9,12 @@ whose K/V already sit in the paged cache in HBM:
   2. one host-to-device copy of the slots and positions;
   3. cache write: the new tokens' K/V to their slots, device block table and
      lengths kept up to date in the same kernel;
-  4. paged decode: the split kernel over the blocks of each sequence, then the
-     merge kernel for sequences split over several chunks.
+  4. paged decode: a plan kernel (prefix sum of blocks per row), the decode
+     kernel (the blocks of all rows divided evenly among the wavefronts of each
+     kv head), and the merge kernel for rows cut between wavefronts.
 ``value`` is the KV bytes every step attends (sum of lengths x kv heads x 128
 x 2 x element bytes) divided by the measured step time.  The line also
-carries the roofline of the dominant kernel (the decode split kernel, timed
+carries the roofline of the dominant kernel (the decode kernel, timed
 with HIP events recorded on its stream by the library around it), and the
 CPU oracle timed on a bounded sample of the same workload.
 
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
-    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--decode-parts", type=int, default=0, help="wavefronts per kv head (0 = auto)")
     ap.add_argument("--context", type=int, default=16384, help="chunked: cached context before the chunk")
     ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"), help="chunked: cache dtype")
     ap.add_argument("--fixed-len", type=int, default=0,
@@ -108,14 +109,14 @@ def run_chunked(args, w, device):
         for e in row:
             e.record(stream)
     mdl = max(lens[:nd])
-    a = pk._args(cache, q, out, table, klens, max(lens), 0, args.split_tokens, None, cu_q=cu_q, num_decode=nd,
+    a = pk._args(cache, q, out, table, klens, max(lens), 0, args.decode_parts, None, cu_q=cu_q, num_decode=nd,
                  max_decode_kv_len=mdl, max_q_len=max(w.q_lens), total_q=q.shape[0])
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
 
     def step(i):
         pk.paged_attn_prefill_chunk(cache, q, cu_q, table, klens, max(lens), nd, max(w.q_lens), out=out,
-                                    max_decode_kv_len=mdl, split_tokens=args.split_tokens, workspace=ws,
+                                    max_decode_kv_len=mdl, decode_parts=args.decode_parts, workspace=ws,
                                     events=[e.cuda_event for e in ev[i]])
 
     for i in range(args.warmup):
@@ -127,7 +128,7 @@ def run_chunked(args, w, device):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     timed = range(args.warmup, total)
-    dec_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in timed]))
+    dec_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in timed]))  # decode + merge
     pre_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in timed]))
     C = max(w.q_lens)
     P = lens[-1] - C
@@ -308,7 +309,7 @@ def main():
     d_io = torch.empty((2, B), dtype=torch.int32, device=device)
     ones = [1] * B
     # workspace sized for the longest row the run reaches
-    a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.split_tokens, None)
+    a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.decode_parts, None)
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
@@ -332,7 +333,7 @@ def main():
         ev[i][0].record(stream)
         pk.kv_cache_write(cache, k_new[i], v_new[i], d_io[0], rows=d_rows, positions=d_io[1],
                           block_table=d_table, kv_lens=d_lens)
-        pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, split_tokens=args.split_tokens,
+        pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, decode_parts=args.decode_parts,
                              workspace=ws, events=[ev[i][1].cuda_event, ev[i][2].cuda_event, ev[i][3].cuda_event])
         kv_bytes_step.append(int(lens.sum()) * w.hkv * w.d * 2 * elt_bytes(w))
 
@@ -349,9 +350,9 @@ def main():
     dt = time.perf_counter() - t0
 
     timed = range(args.warmup, total)
-    split_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]
+    split_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]  # decode kernel
     merge_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in timed]
-    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
+    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]  # cache write + decode plan
     bytes_timed = kv_bytes_step[args.warmup:]
     ms_per_step = dt * 1e3 / args.steps
     value = sum(bytes_timed) / dt / 1e9
@@ -374,15 +375,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(w), "batch": B, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "block_size": 16, "mean_kv_len": round(float(np.mean(lens)), 1),
-                   "pool_blocks": w.num_blocks, "split_tokens": args.split_tokens or "auto",
+                   "pool_blocks": w.num_blocks, "decode_parts": args.decode_parts or "auto",
                    "placement": args.placement},
         "seq_tokens_per_s": round(tokens_per_s, 1),
-        "kernels_us": {"decode_split": round(float(np.mean(split_ms)) * 1e3, 2),
+        "kernels_us": {"decode": round(float(np.mean(split_ms)) * 1e3, 2),
                        "decode_merge": round(float(np.mean(merge_ms)) * 1e3, 2),
-                       "cache_write": round(float(np.mean(write_ms)) * 1e3, 2)},
+                       "cache_write_and_plan": round(float(np.mean(write_ms)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_split_kernel (KV bytes of all rows per launch / event-timed duration)"},
+                     "kernel": "decode_kernel (KV bytes of all rows per launch / event-timed duration)"},
         "copy_on_write_copies": copies_total,
         "host_us_per_step": round(host * 1e6 / args.steps, 1),
     }

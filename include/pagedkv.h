@@ -187,13 +187,16 @@ typedef struct {
     int32_t max_q_len;           /* host: upper bound on the other rows' query counts */
     int32_t total_q;             /* host: cu_q[num_seqs] */
     /* tuning and scratch: */
-    int32_t split_tokens;        /* tokens per split-K chunk, multiple of 16, <= 1024; 0 = auto */
-    void* workspace;             /* device scratch for split-K partials */
+    int32_t decode_parts;        /* decode: the blocks of each kv head are divided evenly among this
+                                    many wavefronts (<= 4096, and at most one per 8 blocks of the
+                                    head's work); 0 = auto (8 per compute unit in all) */
+    void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
-     * the call records on its stream: [0] before its first kernel, [1] after
-     * the decode split kernel, [2] after the decode merge kernel (or where it
-     * would be), [3] after the prefill kernel.  The caller owns the events. */
+     * the call records on its stream: [0] after the decode plan kernel (just
+     * before the decode kernel), [1] after the decode kernel, [2] after the
+     * decode merge kernel, [3] after the prefill kernel.  The caller owns the
+     * events. */
     void* events[4];
 } pkv_attn_args;
 
@@ -205,10 +208,12 @@ int paged_attn_workspace_size(const pkv_cache* cache, const pkv_attn_args* args,
  * the block table ([P3] item (d): the attention kernel reads K/V from
  * non-contiguous blocks through the table); softmax(q K^T / sqrt(d)) V with a
  * running max and normaliser over blocks ([P1] "FlashAttention: why the
- * mechanism this whole layer runs on isn't compute-bound"); long rows are
- * split over the keys and the partial results merged by a second kernel.
- * The arithmetic order depends on logical positions only, so any placement
- * of the blocks gives bit-identical output. */
+ * mechanism this whole layer runs on isn't compute-bound").  The blocks of
+ * all rows are divided evenly among decode_parts wavefronts per kv head; rows
+ * cut between wavefronts are merged by a second kernel.  The arithmetic order
+ * depends on logical positions only, so any placement of the blocks gives
+ * bit-identical output.  A row with an invalid length or an out-of-range
+ * block id gets NaN output. */
 int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
 /* Chunked prefill batched with decode rows ([P1] "Serving systems: the layer

@@ -68,7 +68,7 @@ class pkv_attn_args(ctypes.Structure):
                 ("kv_lens", ctypes.c_void_p), ("max_kv_len", ctypes.c_int32),
                 ("cu_q", ctypes.c_void_p), ("num_decode", ctypes.c_int32),
                 ("max_decode_kv_len", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
-                ("total_q", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("decode_parts", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("events", ctypes.c_void_p * 4)]
 
@@ -352,7 +352,7 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace,
+def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace,
           cu_q=None, num_decode=0, max_decode_kv_len=0, max_q_len=0, total_q=0) -> pkv_attn_args:
     if q.dtype not in _QDT:
         raise PagedKVError(-4, f"query dtype {q.dtype}")
@@ -383,7 +383,7 @@ def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, split
     a.max_decode_kv_len = int(max_decode_kv_len)
     a.max_q_len = int(max_q_len)
     a.total_q = int(total_q)
-    a.split_tokens = split_tokens
+    a.decode_parts = decode_parts
     if workspace is not None:
         a.workspace = workspace.data_ptr()
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -413,12 +413,12 @@ def _set_events(a, events):
 
 
 def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, out=None, layer: int = 0,
-                      split_tokens: int = 0, workspace=None, stream=None, events=None):
+                      decode_parts: int = 0, workspace=None, stream=None, events=None):
     """q [rows, Hq, 128] -> out [rows, Hq, 128] (q's dtype).  ``events``: up to
     four hipEvent_t handles (ints) recorded around the kernels (see the header)."""
     if out is None:
         out = torch.empty_like(q)
-    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace)
+    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace)
     _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841 (alive until enqueued)
     _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
@@ -427,11 +427,11 @@ def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, 
 
 def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_kv_len: int, num_decode: int,
                              max_q_len: int, out=None, layer: int = 0, max_decode_kv_len: int = 0,
-                             split_tokens: int = 0, workspace=None, stream=None, events=None):
+                             decode_parts: int = 0, workspace=None, stream=None, events=None):
     """q [total_q, Hq, 128]; rows 0..num_decode-1 are decode rows (cu_q[i] = i)."""
     if out is None:
         out = torch.empty_like(q)
-    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, split_tokens, workspace, cu_q=cu_q,
+    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace, cu_q=cu_q,
               num_decode=num_decode, max_decode_kv_len=max_decode_kv_len, max_q_len=max_q_len,
               total_q=q.shape[0])
     _set_events(a, events)

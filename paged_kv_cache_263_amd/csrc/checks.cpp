@@ -39,33 +39,13 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
         return fail(PKV_ERR_INVALID, "max_blocks %d / max_kv_len %d must be positive", a->max_blocks, a->max_kv_len);
     if (static_cast<int64_t>(a->max_kv_len) > static_cast<int64_t>(a->max_blocks) * PKV_BLOCK_SIZE)
         return fail(PKV_ERR_INVALID, "max_kv_len %d exceeds max_blocks * 16", a->max_kv_len);
-    if (a->split_tokens != 0 && (a->split_tokens % PKV_BLOCK_SIZE != 0 || a->split_tokens < 16 || a->split_tokens > 1024))
-        return fail(PKV_ERR_INVALID, "split_tokens %d must be 0 or a multiple of 16 in [16, 1024]", a->split_tokens);
+    if (a->decode_parts < 0 || a->decode_parts > 4096)
+        return fail(PKV_ERR_INVALID, "decode_parts %d must be in [0, 4096]", a->decode_parts);
     const uintptr_t align = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->out) |
                             reinterpret_cast<uintptr_t>(c->k_pool) | reinterpret_cast<uintptr_t>(c->v_pool) |
                             reinterpret_cast<uintptr_t>(a->workspace);
     if (align & 15u) return fail(PKV_ERR_INVALID, "q, out, pools and workspace must be 16-byte aligned");
     return PKV_OK;
-}
-
-int32_t decode_split_tokens(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len) {
-    if (a->split_tokens) return a->split_tokens;
-    // The largest chunk that still gives ~8K work items (32 per CU): long rows
-    // get long chunks (fewer partial results to write and merge), short
-    // batches get short ones (enough work items to fill 256 CUs).
-    const int64_t pairs = static_cast<int64_t>(rows) * c->num_kv_heads;
-    for (int32_t st : {1024, 512, 256, 128}) {
-        if (pairs * ((max_kv_len + st - 1) / st) >= 8192) return st;
-    }
-    return 64;
-}
-
-size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len) {
-    if (rows <= 0) return 0;
-    const int32_t st = decode_split_tokens(c, a, rows, max_kv_len);
-    const int64_t splits = (max_kv_len + st - 1) / st;
-    if (splits <= 1) return 0;
-    return static_cast<size_t>(rows) * a->num_q_heads * splits * (PKV_HEAD_DIM + 2) * sizeof(float);
 }
 
 }  // namespace pkv

@@ -1,6 +1,8 @@
-// Paged GQA decode on gfx950: one wavefront per (row, kv head, key chunk)
-// streams the chunk's 16-token blocks through the block table, and a second
-// kernel merges the chunks of rows that were split.
+// Paged GQA decode on gfx950.  The decode work of one kv head - every block of
+// every row, in row order - is divided into equal contiguous ranges of blocks,
+// one per wavefront; a wavefront streams its range's 16-token blocks through
+// the block table, and a merge kernel combines the pieces of rows that were
+// divided between wavefronts.
 //
 // What is computed: softmax(q K^T / sqrt(d)) V for one query per row over the
 // row's cached tokens, K/V read from scattered blocks through the table ([P3]
@@ -18,17 +20,28 @@
 // and head (i % 16) of the B operand and of the result, so scores, softmax
 // state and output of head i % 16 stay in the lanes that own that head: the
 // only cross-lane traffic is the max and sum over the four 16-lane groups
-// (two xor shuffles).  With K stored [tok][d] and V stored [d][tok] inside a
-// block, every lane's operand is one contiguous 16 / 8 / 4-byte load and a
-// wave reads each 4 KiB (bf16) tile in whole cache lines.  P is split into a
-// bf16 high part and a bf16 remainder, so P.V keeps ~16 mantissa bits.
-// fp32 caches use the fp32 matrix instruction (16x16x4) with the same lanes;
-// fp8 caches convert E4M3 bytes to bf16 in registers (exact) and fold the
-// per-head scales into the score scale (K) and the final normalisation (V).
+// (two xor shuffles, only when the running maximum moves).  With K stored
+// [tok][d] and V stored [d][tok] inside a block, every lane's operand is one
+// contiguous 16 / 8 / 4-byte load and a wave reads each 4 KiB (bf16) tile in
+// whole cache lines.  P is split into a bf16 high part and a bf16 remainder,
+// so P.V keeps ~16 mantissa bits.  fp32 caches use the fp32 matrix
+// instruction (16x16x4) with the same lanes; fp8 caches convert E4M3 bytes
+// to bf16 in registers (exact) and fold the per-head scales into the score
+// scale (K) and the final normalisation (V).
 //
-// The order of every sum depends on logical token positions only (fixed
-// chunk boundaries, fixed merge order), so a permutation of the physical
-// blocks changes no bit of the output.
+// Work division.  Rows have very different lengths, so fixed-size chunks per
+// row leave some wavefronts long tails of work while others sit idle.  Here
+// a plan kernel turns the row lengths into a prefix sum of blocks per row;
+// for kv head h, wavefront i of Q takes blocks [floor(i U / Q), floor((i+1) U
+// / Q)) of the U blocks of all rows in row order, so every wavefront streams
+// the same number of blocks (within one).  A row entirely inside one range is
+// finished and written by that wavefront; a row cut by range boundaries is
+// left as partial results (running max, normaliser, unnormalised output) -
+// at most two per wavefront, one for the row at each end of its range - and
+// the merge kernel combines them in wavefront order.  The partition depends
+// on the lengths only, so every sum is taken in an order fixed by logical
+// positions and a permutation of the physical blocks changes no bit of the
+// output.
 #include <cmath>
 #include <cstdlib>
 
@@ -39,19 +52,36 @@ namespace pkv {
 namespace {
 
 struct DecodeParams {
-    const void* q;            // [rows][hq][128]
-    void* out;                // [rows][hq][128]
-    const void* k_pool;       // this layer: [num_blocks][hkv][16][128]
-    const void* v_pool;       // this layer: [num_blocks][hkv][128][16]
-    const float* k_scale;     // this layer: [hkv] (fp8 only)
+    const void* q;                  // [rows][hq][128]
+    void* out;                      // [rows][hq][128]
+    const void* k_pool;             // this layer: [num_blocks][hkv][16][128]
+    const void* v_pool;             // this layer: [num_blocks][hkv][128][16]
+    const float* k_scale;           // this layer: [hkv] (fp8 only)
     const float* v_scale;
-    const int32_t* table;     // [rows][max_blocks]
-    const int32_t* kv_lens;   // [rows]
-    float* ws_acc;            // [rows][hq][max_splits][128]
-    float* ws_ml;             // [rows][hq][max_splits][2]
-    int32_t num_blocks, hkv, hq, group, max_blocks, max_kv_len, split_tokens, max_splits;
-    float scale_log2;         // log2(e) / sqrt(d)
+    const int32_t* __restrict__ table;    // [rows][max_blocks]
+    const int32_t* __restrict__ kv_lens;  // [rows]
+    int32_t* plan;                  // [rows + 1]: blocks of rows 0..b-1 (0 blocks for an invalid row)
+    float* ws_acc;                  // [hkv][Q][2][group][128] partial unnormalised outputs
+    float* ws_ml;                   // [hkv][Q][2][group][2] partial (max, normaliser)
+    int32_t rows, num_blocks, hkv, hq, group, max_blocks, max_kv_len, parts;  // parts = Q
+    float scale_log2;               // log2(e) / sqrt(d)
 };
+
+__device__ __forceinline__ bool row_valid(int L, const DecodeParams& p) {
+    return L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS;
+}
+
+// First block of wavefront i's range for a head with U blocks over Q parts.
+__device__ __forceinline__ int64_t range_start(int64_t U, int i, int Q) { return U * i / Q; }
+
+// Parts actually used: at most one per kMinBlocks blocks, so that no range is
+// empty (every wavefront that has a range writes its pieces) and tiny batches
+// are not cut into one-block pieces.
+constexpr int kMinBlocks = 8;
+__device__ __forceinline__ int effective_parts(int64_t U, int parts) {
+    const int64_t q = U / kMinBlocks;
+    return static_cast<int>(q < 1 ? 1 : (q < parts ? q : parts));
+}
 
 template <int QT>
 __device__ __forceinline__ void store_out4(void* out, int64_t qrow, int d, f32x4_t v) {
@@ -266,145 +296,218 @@ struct Online {
     }
 };
 
+// Plan: prefix sum of blocks per row (invalid rows count 0 blocks and get NaN
+// output here).  One workgroup of 1024 threads, rows in chunks of 1024.
+template <int QT>
+__global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p) {
+    __shared__ int32_t wsum[16];
+    __shared__ int32_t carry_sh;
+    const int t = threadIdx.x;
+    if (t == 0) {
+        carry_sh = 0;
+        p.plan[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < p.rows; base += 1024) {
+        const int b = base + t;
+        int nb = 0;
+        bool invalid = false;
+        if (b < p.rows) {
+            const int L = p.kv_lens[b];
+            invalid = !row_valid(L, p);
+            nb = invalid ? 0 : (L + kBS - 1) / kBS;
+        }
+        // inclusive scan: within the wave, then across the 16 waves
+        int v = nb;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(v, off);
+            if ((t & 63) >= off) v += u;
+        }
+        if ((t & 63) == 63) wsum[t >> 6] = v;
+        __syncthreads();
+        int add = carry_sh;
+        for (int w = 0; w < (t >> 6); ++w) add += wsum[w];
+        if (b < p.rows) p.plan[b + 1] = v + add;
+        __syncthreads();
+        if (t == 1023) carry_sh = v + add;
+        __syncthreads();
+        if (invalid) {  // the whole row becomes NaN
+            const float nan = __builtin_nanf("");
+            for (int e = 0; e < p.hq * kD; ++e) {
+                if constexpr (QT == PKV_F32)
+                    static_cast<float*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = nan;
+                else
+                    static_cast<uint16_t*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = 0x7FC0u;
+            }
+        }
+    }
+}
+
+// Index of the row holding block position x: plan[b] <= x < plan[b+1].
+__device__ __forceinline__ int find_row(const int32_t* plan, int rows, int64_t x) {
+    int lo = 0, hi = rows;  // invariant: plan[lo] <= x < plan[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (plan[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 template <int KV, int NBUF>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
     using Elt = typename Tile<KV>::Elt;
     const int lane = threadIdx.x;
     const int r = lane & 15;
     const int g = lane >> 4;
-    // blockIdx -> (row, split, kv head); kv head fastest so that consecutive
-    // workgroups (dealt round-robin to the 8 XCDs) keep one kv head per XCD.
-    const int per_row = p.max_splits * p.hkv;
-    const int row = blockIdx.x / per_row;
-    const int rem = blockIdx.x - row * per_row;
-    const int split = rem / p.hkv;
-    const int kvh = rem - split * p.hkv;
-
-    const int L = p.kv_lens[row];
-    const bool row_ok = L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS;
-    const int nsplit = row_ok ? (L + p.split_tokens - 1) / p.split_tokens : 1;
-    if (split >= nsplit) return;
+    // kv head fastest: consecutive workgroups are dealt round-robin to the 8
+    // XCDs, so with 8 kv heads each XCD streams one head (and keeps that
+    // head's shared-prefix blocks in its own L2).
+    const int kvh = blockIdx.x % p.hkv;
+    const int wi = blockIdx.x / p.hkv;
+    const int64_t U = p.plan[p.rows];
+    const int Q = effective_parts(U, p.parts);
+    if (wi >= Q || U <= 0) return;
+    const int64_t u0 = range_start(U, wi, Q);
+    const int64_t u1 = range_start(U, wi + 1, Q);
+    if (u0 >= u1) return;
     const bool head_ok = r < p.group;
-    const int64_t qrow = static_cast<int64_t>(row) * p.hq + kvh * p.group + (head_ok ? r : 0);
     const float nan = __builtin_nanf("");
     const f32x4_t nan4 = {nan, nan, nan, nan};
 
-    const int t0 = split * p.split_tokens;
-    const int t1 = min(L, t0 + p.split_tokens);
-    const int nblk = row_ok ? (t1 - t0 + kBS - 1) / kBS : 0;
-    const int32_t* trow = p.table + static_cast<int64_t>(row) * p.max_blocks + t0 / kBS;
-    const int tb = lane < nblk ? trow[lane] : 0;
-    const bool bad = !row_ok || __any(lane < nblk && (tb < 0 || tb >= p.num_blocks));
-    if (bad) {  // invalid row or block id: the row's output becomes NaN
-        if (!head_ok) return;
-        if (nsplit == 1) {
-#pragma unroll
-            for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, nan4);
-        } else {
-            const int64_t w = qrow * p.max_splits + split;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) st<f32x4_t>(p.ws_acc + w * kD + 16 * n + 4 * g, nan4);
-            if (g == 0) st<float2>(p.ws_ml + 2 * w, float2{0.f, nan});
-        }
-        return;
-    }
-
     float scale = p.scale_log2;
-    if constexpr (KV == PKV_FP8_E4M3) scale *= p.k_scale[kvh];
-
+    float vs = 1.f;
+    if constexpr (KV == PKV_FP8_E4M3) {
+        scale *= p.k_scale[kvh];
+        vs = p.v_scale[kvh];
+    }
     const Elt* kpool = static_cast<const Elt*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile;
     const Elt* vpool = static_cast<const Elt*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile;
     const int64_t blk_stride = static_cast<int64_t>(p.hkv) * kTile;
 
-    typename Tile<KV>::Q q;
-    Tile<KV>::load_q(q, static_cast<const char*>(p.q) + qrow * kD * kQBytes, head_ok, g);
+    int b = find_row(p.plan, p.rows, u0);
+    const int b_first = b;
+    for (int64_t u = u0; u < u1; ++b) {
+        const int64_t rb0 = p.plan[b];
+        const int64_t rb1 = p.plan[b + 1];
+        if (rb1 <= u) continue;  // a row with no blocks
+        const int L = p.kv_lens[b];
+        const int j0 = static_cast<int>(u - rb0);
+        const int j1 = static_cast<int>((u1 < rb1 ? u1 : rb1) - rb0);
+        const int t0 = j0 * kBS;
+        const int t1 = min(L, j1 * kBS);
+        const int nblk = j1 - j0;
+        const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * p.group + (head_ok ? r : 0);
+        const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks + j0;
 
-    Online o;
-    // Ring of NBUF register tiles: while block j is computed, blocks
-    // j+1 .. j+NBUF-1 are in flight.  The trip count is padded to a multiple
-    // of NBUF and every load is unconditional (block index clamped to the
-    // last block, a cache hit), so no branch sits between a load and its use
-    // and the compiler's wait counts let the prefetched loads stay in flight.
-    // Padding steps are fully masked and change nothing.
-    const int niter = (nblk + NBUF - 1) / NBUF * NBUF;
-    auto tile_off = [&](int j) -> int64_t {
-        return static_cast<int64_t>(__builtin_amdgcn_readlane(tb, min(j, nblk - 1))) * blk_stride;
-    };
-    Tile<KV> t[NBUF];
+        typename Tile<KV>::Q q;
+        Tile<KV>::load_q(q, static_cast<const char*>(p.q) + qrow * kD * kQBytes, head_ok, g);
+
+        // Ring of NBUF register tiles: while block j is computed, blocks
+        // j+1 .. j+NBUF-1 are in flight.  The trip count is padded to a
+        // multiple of NBUF and every load is unconditional (block index
+        // clamped to the piece's last block, a cache hit), so no branch sits
+        // between a load and its use and the wait counts keep the prefetched
+        // loads in flight.  Padding steps are fully masked and change nothing.
+        // A block id outside the pool is replaced by block 0 and marks the
+        // piece bad (its output becomes NaN).
+        bool bad = false;
+        auto tile_off = [&](int j) -> int64_t {
+            int32_t id = trow[min(j, nblk - 1)];
+            const bool ok = id >= 0 && id < p.num_blocks;
+            bad = bad || !ok;
+            return static_cast<int64_t>(ok ? id : 0) * blk_stride;
+        };
+        Online o;
+        const int niter = (nblk + NBUF - 1) / NBUF * NBUF;
+        Tile<KV> t[NBUF];
 #pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) {
-        const int64_t b = tile_off(u);
-        t[u].load(kpool + b, vpool + b, r, g);
-    }
-    for (int j0 = 0; j0 < niter; j0 += NBUF) {
-#pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-            const int j = j0 + u;
-            const int64_t b = tile_off(j + NBUF - 1);
-            t[(u + NBUF - 1) % NBUF].load(kpool + b, vpool + b, r, g);
-            o.step<KV>(t[u], q, scale, t0 + j * kBS + 4 * g, t1, t0 + (j + 1) * kBS);
+        for (int v = 0; v < NBUF - 1; ++v) {
+            const int64_t off = tile_off(v);
+            t[v].load(kpool + off, vpool + off, r, g);
         }
-    }
+        for (int jb = 0; jb < niter; jb += NBUF) {
+#pragma unroll
+            for (int v = 0; v < NBUF; ++v) {
+                const int j = jb + v;
+                const int64_t off = tile_off(j + NBUF - 1);
+                t[(v + NBUF - 1) % NBUF].load(kpool + off, vpool + off, r, g);
+                o.step<KV>(t[v], q, scale, t0 + j * kBS + 4 * g, t1, t0 + (j + 1) * kBS);
+            }
+        }
 
-    float l = o.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    float vs = 1.f;
-    if constexpr (KV == PKV_FP8_E4M3) vs = p.v_scale[kvh];
-    if (!head_ok) return;
-    if (nsplit == 1) {
-        const float inv = vs / l;
+        float l = o.l;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const bool whole = rb0 >= u0 && rb1 <= u1;  // no other wavefront touches this row
+        if (head_ok) {
+            if (whole) {
+                const float inv = bad ? nan : vs / l;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, o.acc[n] * inv);
-    } else {
-        const int64_t w = qrow * p.max_splits + split;
+                for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, o.acc[n] * inv);
+            } else {
+                const int side = (b == b_first) ? 0 : 1;
+                const int64_t w = ((static_cast<int64_t>(kvh) * p.parts + wi) * 2 + side) * p.group + r;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) st<f32x4_t>(p.ws_acc + w * kD + 16 * n + 4 * g, o.acc[n] * vs);
-        if (g == 0) st<float2>(p.ws_ml + 2 * w, float2{o.m, l});
+                for (int n = 0; n < 8; ++n)
+                    st<f32x4_t>(p.ws_acc + w * kD + 16 * n + 4 * g, bad ? nan4 : o.acc[n] * vs);
+                if (g == 0) st<float2>(p.ws_ml + 2 * w, float2{o.m, bad ? nan : l});
+            }
+        }
+        u = rb1 < u1 ? rb1 : u1;
     }
 }
 
-// Merge the chunks of one (row, query head): out = sum_i acc_i 2^(m_i - M) /
-// sum_i l_i 2^(m_i - M), M = max_i m_i.  The weights are computed once into
-// LDS; each lane (one per d) then sums the chunks in chunk order.
-constexpr int kMaxSplits = 4096;
+// Merge the pieces of one (row, query head) that was divided between
+// wavefronts: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
+// M = max_i m_i, in wavefront order.  The weights are computed once into LDS;
+// each lane (one per d) then sums the pieces.
+constexpr int kMaxParts = 4096;
 template <int QT>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p) {
-    __shared__ float wsh[kMaxSplits];
+    __shared__ float wsh[kMaxParts];
     __shared__ float red[2];
     const int64_t qrow = blockIdx.x;
-    const int row = static_cast<int>(qrow / p.hq);
+    const int b = static_cast<int>(qrow / p.hq);
+    const int hq = static_cast<int>(qrow % p.hq);
+    const int kvh = hq / p.group;
+    const int hh = hq % p.group;
     const int d = threadIdx.x;
-    const int L = p.kv_lens[row];
-    const bool row_ok = L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS;
-    const int nsplit = row_ok ? (L + p.split_tokens - 1) / p.split_tokens : 1;
-    if (nsplit <= 1) return;
-    const float* ml = p.ws_ml + 2 * qrow * p.max_splits;
+    const int64_t U = p.plan[p.rows];
+    const int64_t rb0 = p.plan[b];
+    const int64_t rb1 = p.plan[b + 1];
+    if (rb1 <= rb0 || U <= 0) return;  // invalid row (NaN written by the plan kernel)
+    const int Q = effective_parts(U, p.parts);
+    // wavefronts whose ranges meet [rb0, rb1)
+    int i0 = static_cast<int>(rb0 * Q / U);
+    while (i0 + 1 < Q && range_start(U, i0 + 1, Q) <= rb0) ++i0;
+    while (i0 > 0 && range_start(U, i0, Q) > rb0) --i0;
+    int i1 = static_cast<int>((rb1 - 1) * Q / U);
+    while (i1 + 1 < Q && range_start(U, i1 + 1, Q) <= rb1 - 1) ++i1;
+    while (i1 > 0 && range_start(U, i1, Q) > rb1 - 1) --i1;
+    if (i0 == i1) return;  // written directly by the one wavefront
+    const int n = i1 - i0 + 1;
+    auto slot = [&](int k) -> int64_t {
+        const int i = i0 + k;
+        const int side = range_start(U, i, Q) < rb0 ? 1 : 0;
+        return ((static_cast<int64_t>(kvh) * p.parts + i) * 2 + side) * p.group + hh;
+    };
     float mx = -INFINITY;
-    for (int i = d; i < nsplit; i += 128) mx = fmaxf(mx, ml[2 * i]);
+    for (int k = d; k < n; k += 128) mx = fmaxf(mx, p.ws_ml[2 * slot(k)]);
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if ((d & 63) == 0) red[d >> 6] = mx;
     __syncthreads();
     mx = fmaxf(red[0], red[1]);
-    for (int i = d; i < nsplit; i += 128) wsh[i] = __builtin_amdgcn_exp2f(ml[2 * i] - mx);
+    for (int k = d; k < n; k += 128) wsh[k] = __builtin_amdgcn_exp2f(p.ws_ml[2 * slot(k)] - mx);
     __syncthreads();
-    // denominator in chunk order (every lane computes the same sum)
-    float den = 0.f;
-    for (int i = 0; i < nsplit; ++i) den += ml[2 * i + 1] * wsh[i];
-    const float* acc = p.ws_acc + qrow * p.max_splits * kD + d;
-    float num = 0.f;
-    int i = 0;
-    for (; i + 4 <= nsplit; i += 4) {
-        const float a0 = acc[static_cast<int64_t>(i) * kD], a1 = acc[static_cast<int64_t>(i + 1) * kD];
-        const float a2 = acc[static_cast<int64_t>(i + 2) * kD], a3 = acc[static_cast<int64_t>(i + 3) * kD];
-        num += a0 * wsh[i];
-        num += a1 * wsh[i + 1];
-        num += a2 * wsh[i + 2];
-        num += a3 * wsh[i + 3];
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < n; ++k) {
+        const int64_t sl = slot(k);
+        num += p.ws_acc[sl * kD + d] * wsh[k];
+        den += p.ws_ml[2 * sl + 1] * wsh[k];
     }
-    for (; i < nsplit; ++i) num += acc[static_cast<int64_t>(i) * kD] * wsh[i];
     const float o = num / den;
     if constexpr (QT == PKV_F32) {
         static_cast<float*>(p.out)[qrow * kD + d] = o;
@@ -418,32 +521,63 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
 int decode_pipeline_depth() {
     static const int depth = [] {
         const char* e = std::getenv("PKV_DECODE_DEPTH");
-        const int v = e ? std::atoi(e) : 3;
+        const int v = e ? std::atoi(e) : 2;
         return v < 2 ? 2 : (v > 4 ? 4 : v);
     }();
     return depth;
 }
 
+// Wavefronts per kv head: PKV_DECODE_WAVES_PER_CU wavefronts per compute
+// unit in total (default 8), shared among the kv heads.
+int decode_parts_auto(int hkv) {
+    static const int per_cu = [] {
+        const char* e = std::getenv("PKV_DECODE_WAVES_PER_CU");
+        const int v = e ? std::atoi(e) : 8;
+        return v < 1 ? 1 : (v > 32 ? 32 : v);
+    }();
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    const int parts = (cus * per_cu + hkv - 1) / hkv;
+    return parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts);
+}
+
 }  // namespace
+
+int32_t decode_parts(const pkv_cache* c, const pkv_attn_args* a) {
+    if (a->decode_parts > 0) return a->decode_parts < kMaxParts ? a->decode_parts : kMaxParts;
+    return decode_parts_auto(c->num_kv_heads);
+}
+
+size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {
+    if (rows <= 0) return 0;
+    const int64_t Q = decode_parts(c, a);
+    const int64_t group = a->num_q_heads / c->num_kv_heads;
+    const int64_t plan = (static_cast<int64_t>(rows) + 1 + 3) / 4 * 4;  // int32, 16-byte multiple
+    const int64_t slots = static_cast<int64_t>(c->num_kv_heads) * Q * 2 * group;
+    return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4);
+}
 
 // Launch decode over `rows` rows whose q/out/table/kv_lens start at the given
 // pointers (used by paged_attn_decode and by the decode rows of a prefill call).
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
                   hipStream_t stream) {
+    auto mark = [&](int i) {
+        if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
+    };
     if (rows <= 0) {
-        for (int i = 0; i < 3; ++i)
-            if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
+        for (int i = 0; i < 3; ++i) mark(i);
         return PKV_OK;
     }
-    const int32_t st_tokens = decode_split_tokens(c, a, rows, max_kv_len);
-    const int32_t splits = (max_kv_len + st_tokens - 1) / st_tokens;
-    const size_t need = decode_workspace_bytes(c, a, rows, max_kv_len);
-    if (need > 0 && (!workspace || ws_bytes < need))
+    const size_t need = decode_workspace_bytes(c, a, rows);
+    if (!workspace || ws_bytes < need)
         return fail(PKV_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? ws_bytes : 0);
-    if (splits > kMaxSplits) return fail(PKV_ERR_INVALID, "more than %d key chunks per row", kMaxSplits);
-    const int64_t grid = static_cast<int64_t>(rows) * splits * c->num_kv_heads;
-    if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "decode launch too large");
+    const int32_t Q = decode_parts(c, a);
+    const int64_t grid = static_cast<int64_t>(Q) * c->num_kv_heads;
 
     const int64_t elt = c->kv_dtype == PKV_F32 ? 4 : c->kv_dtype == PKV_BF16 ? 2 : 1;
     const int64_t layer_elems = static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * kTile;
@@ -456,48 +590,50 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.v_scale = c->v_scale ? c->v_scale + static_cast<int64_t>(a->layer) * c->num_kv_heads : nullptr;
     p.table = table;
     p.kv_lens = kv_lens;
-    const int64_t accs = static_cast<int64_t>(rows) * a->num_q_heads * splits * kD;
-    p.ws_acc = need ? static_cast<float*>(workspace) : nullptr;
-    p.ws_ml = need ? static_cast<float*>(workspace) + accs : nullptr;
+    const int64_t plan_ints = (static_cast<int64_t>(rows) + 1 + 3) / 4 * 4;
+    const int64_t slots = static_cast<int64_t>(c->num_kv_heads) * Q * 2 * (a->num_q_heads / c->num_kv_heads);
+    p.plan = static_cast<int32_t*>(workspace);
+    p.ws_acc = reinterpret_cast<float*>(static_cast<int32_t*>(workspace) + plan_ints);
+    p.ws_ml = p.ws_acc + slots * kD;
+    p.rows = rows;
     p.num_blocks = c->num_blocks;
     p.hkv = c->num_kv_heads;
     p.hq = a->num_q_heads;
     p.group = a->num_q_heads / c->num_kv_heads;
     p.max_blocks = a->max_blocks;
     p.max_kv_len = max_kv_len;
-    p.split_tokens = st_tokens;
-    p.max_splits = splits;
+    p.parts = Q;
     p.scale_log2 = kLog2e / sqrtf(static_cast<float>(kD));
 
-    auto mark = [&](int i) {
-        if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
-    };
+    const bool f32 = a->q_dtype == PKV_F32;
+    if (f32)
+        hipLaunchKernelGGL(decode_plan_kernel<PKV_F32>, dim3(1), dim3(1024), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_plan_kernel<PKV_BF16>, dim3(1), dim3(1024), 0, stream, p);
     mark(0);
     const dim3 g1(static_cast<unsigned>(grid));
     const int depth = decode_pipeline_depth();
     switch (c->kv_dtype) {
         case PKV_F32:
-            hipLaunchKernelGGL((decode_split_kernel<PKV_F32, 2>), g1, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_F32, 2>), g1, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
-            if (depth <= 2) hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 2>), g1, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 3>), g1, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_split_kernel<PKV_BF16, 4>), g1, dim3(64), 0, stream, p);
+            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 2>), g1, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 3>), g1, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_kernel<PKV_BF16, 4>), g1, dim3(64), 0, stream, p);
             break;
         default:
-            if (depth <= 2) hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 2>), g1, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 3>), g1, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_split_kernel<PKV_FP8_E4M3, 4>), g1, dim3(64), 0, stream, p);
+            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 2>), g1, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 3>), g1, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 4>), g1, dim3(64), 0, stream, p);
             break;
     }
     mark(1);
-    if (splits > 1) {
-        const int64_t mgrid = static_cast<int64_t>(rows) * a->num_q_heads;
-        if (a->q_dtype == PKV_F32)
-            hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, dim3(static_cast<unsigned>(mgrid)), dim3(128), 0, stream, p);
-        else
-            hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, dim3(static_cast<unsigned>(mgrid)), dim3(128), 0, stream, p);
-    }
+    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * a->num_q_heads));
+    if (f32)
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, dim3(128), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, dim3(128), 0, stream, p);
     mark(2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -517,8 +653,7 @@ int paged_attn_workspace_size(const pkv_cache* c, const pkv_attn_args* a, size_t
     // A prefill call uses the decode path for its decode rows; its chunk rows
     // need no workspace.
     const int32_t rows = a->cu_q ? a->num_decode : a->num_seqs;
-    const int32_t len = (a->cu_q && a->max_decode_kv_len > 0) ? a->max_decode_kv_len : a->max_kv_len;
-    *bytes = pkv::decode_workspace_bytes(c, a, rows, len);
+    *bytes = pkv::decode_workspace_bytes(c, a, rows);
     return PKV_OK;
 }
 

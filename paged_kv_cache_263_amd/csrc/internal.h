@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdarg>
+#include <cstddef>
 #include <cstdint>
 
 #include "pagedkv.h"
@@ -15,10 +16,10 @@ int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)))
 int check_cache(const pkv_cache* c);
 int check_attn(const pkv_cache* c, const pkv_attn_args* a);
 
-// Tokens per split-K chunk for a decode launch.
-int32_t decode_split_tokens(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len);
+// Wavefronts per kv head for a decode launch.
+int32_t decode_parts(const pkv_cache* c, const pkv_attn_args* a);
 
-// Workspace the decode part of a call needs (bytes; 0 when no row is split).
-size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len);
+// Workspace the decode part of a call needs (bytes; 0 when it has no rows).
+size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows);
 
 }  // namespace pkv

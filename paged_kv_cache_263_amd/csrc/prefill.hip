@@ -62,18 +62,20 @@ struct PrefillParams {
     float scale_log2;
 };
 
+// Split 8 probabilities into bf16 high parts (truncated) and bf16 remainders,
+// packed as two MFMA operands; v_perm_b32 picks the upper halves of two fp32
+// values into one register (bytes 2,3 of the second source, then of the first).
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
 __device__ __forceinline__ void split_p8(const float p[8], bf16x8_t& hi, bf16x8_t& lo) {
-    uint32_t h[8], l[8];
+    float r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t u = __float_as_uint(p[i]);
-        h[i] = u & 0xFFFF0000u;
-        l[i] = __float_as_uint(p[i] - __uint_as_float(h[i])) & 0xFFFF0000u;
-    }
-    hi = __builtin_bit_cast(bf16x8_t, u32x4_t{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3], (h[4] >> 16) | h[5],
-                                              (h[6] >> 16) | h[7]});
-    lo = __builtin_bit_cast(bf16x8_t, u32x4_t{(l[0] >> 16) | l[1], (l[2] >> 16) | l[3], (l[4] >> 16) | l[5],
-                                              (l[6] >> 16) | l[7]});
+    for (int i = 0; i < 8; ++i) r[i] = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
+    hi = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_hi16(p[0], p[1]), pack_hi16(p[2], p[3]), pack_hi16(p[4], p[5]),
+                                              pack_hi16(p[6], p[7])});
+    lo = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_hi16(r[0], r[1]), pack_hi16(r[2], r[3]), pack_hi16(r[4], r[5]),
+                                              pack_hi16(r[6], r[7])});
 }
 
 // Staging registers for one iteration: thread t owns chunk t of each of the 4
@@ -254,8 +256,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
                     s[nt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nt][k4], s[nt][b], 0, 0, 0);
             }
         }
-        // online softmax per head tile
-        const bool need_mask = kbase + kKeys - 1 > P + j0;  // some key may pass a query of this tile
+        // online softmax per head tile.  Scores stay unscaled until the
+        // exponent (scale > 0, so the maximum commutes with it); keys can pass
+        // a query's position only in the iterations that reach the diagonal,
+        // so only those take the masked path (a uniform branch).
+        const bool need_mask = kbase + kKeys - 1 > P + j0;
         bf16x8_t phi[NT][2], plo[NT][2];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -263,14 +268,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kbase + 16 * b + 4 * g + i;
-                    const float v = s[nt][b][i] * scale;
-                    x[4 * b + i] = (!need_mask || key <= qpos) ? v : -INFINITY;
-                }
-            float mb = x[0];
+                for (int i = 0; i < 4; ++i) x[4 * b + i] = s[nt][b][i];
+            if (need_mask) {
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mb = fmaxf(mb, x[i]);
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (kbase + 16 * b + 4 * g + i > qpos) x[4 * b + i] = -INFINITY;
+            }
+            float mb = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+            for (int i = 3; i < 16; i += 2) mb = fmaxf(fmaxf(mb, x[i]), x[i + 1 < 16 ? i + 1 : i]);
+            mb *= scale;
             // lazy rescale (as in the decode kernel): only when some score
             // passes the reference max by more than kLazy
             if (__any(mb > m[nt] + kLazy)) {
@@ -283,22 +292,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
                 for (int i = 0; i < 8; ++i) acc[nt][i] *= alpha;
                 m[nt] = mn;
             }
+            const float neg_m = -m[nt];
             float pr[16];
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                pr[i] = __builtin_amdgcn_exp2f(x[i] - m[nt]);
+                pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale, neg_m));
                 sum += pr[i];
             }
             l[nt] += sum;
             // k-step h covers blocks 2h, 2h+1: this lane's 8 keys are
             // (block 2h: 4g..4g+3, block 2h+1: 4g..4g+3)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float q8[8] = {pr[8 * h + 0], pr[8 * h + 1], pr[8 * h + 2], pr[8 * h + 3],
-                                     pr[8 * h + 4], pr[8 * h + 5], pr[8 * h + 6], pr[8 * h + 7]};
-                split_p8(q8, phi[nt][h], plo[nt][h]);
-            }
+            for (int h = 0; h < 2; ++h) split_p8(pr + 8 * h, phi[nt][h], plo[nt][h]);
         }
         // O^T += V^T . P^T
 #pragma unroll

@@ -108,14 +108,17 @@ def test_fp8_codes_bit_exact():
             assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
 
 
-def test_split_sizes_agree_and_are_deterministic():
+def test_partitions_agree_and_are_deterministic():
+    """Any number of wavefronts per kv head (1: one wavefront per head walks
+    every row; many: rows cut into pieces and merged) gives the oracle's result,
+    and the same bits on every run."""
     w = W.llama8b(batch=16, variant="peaked", seed=41)
     hip = HipSide(w)
     outs = {}
-    for st in (0, 16, 48, 256, 1024):
-        _, outs[st] = check_decode(w, hip=hip, split_tokens=st)
-        again = hip.decode(split_tokens=st)
-        assert torch.equal(outs[st], again), f"split {st} not deterministic"
+    for parts in (0, 1, 3, 17, 64, 600, 4096):
+        _, outs[parts] = check_decode(w, hip=hip, decode_parts=parts)
+        again = hip.decode(decode_parts=parts)
+        assert torch.equal(outs[parts], again), f"{parts} parts not deterministic"
 
 
 def test_placement_invariance_bitwise():
@@ -163,7 +166,7 @@ def test_copy_on_write_isolation():
     compare(out[1].float().cpu().numpy(), ref, TOL["bf16"], "cow child")
 
 
-def test_invalid_rows_give_nan_and_leave_others_alone():
+def test_invalid_rows_give_nan_and_others_stay_right():
     import paged_kv_cache_263_amd as pk
 
     case("invalid rows")
@@ -177,7 +180,13 @@ def test_invalid_rows_give_nan_and_leave_others_alone():
     out = pk.paged_attn_decode(hip.cache, hip.q, table, lens, hip.max_kv_len)
     torch.cuda.synchronize()
     assert torch.isnan(out[1].float()).all() and torch.isnan(out[2].float()).all()
-    assert torch.equal(out[0], good[0]) and torch.equal(out[3], good[3])
+    # the other rows are still right (not necessarily the same bits: the even
+    # division of the work depends on every row's length)
+    orc = OracleSide(w)
+    for b in (0, 3):
+        assert torch.isfinite(out[b].float()).all()
+        compare(out[b].float().cpu().numpy(), orc.decode(b), TOL["bf16"], f"valid row {b}")
+    del good
 
 
 def test_device_table_upkeep_matches_host_tables():
