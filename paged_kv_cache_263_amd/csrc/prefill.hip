@@ -18,7 +18,7 @@
 // operand reads free of bank conflicts - double buffered, one barrier per
 // iteration.  Each wave then computes, per head tile (16 tokens of one head):
 //   S^T[64 keys x 16 tokens] = K . Q^T           (16 x mfma 16x16x32 bf16)
-//   O^T[128 x 16 tokens]    += V^T . P^T         (8 d-tiles x 2 key halves, P as bf16 hi + lo)
+//   O^T[128 x 16 tokens]    += V^T . P^T         (8 d-tiles x 2 key halves, P rounded to bf16)
 // with the running max / normaliser of the decode kernel (rescaled lazily,
 // only when a score passes the reference max by 2^8) and the causal mask
 // applied only where a key can pass a query's position.  For P.V the 32 keys
@@ -62,62 +62,54 @@ struct PrefillParams {
     float scale_log2;
 };
 
-// Split 8 probabilities into bf16 high parts (truncated) and bf16 remainders,
-// packed as two MFMA operands; v_perm_b32 picks the upper halves of two fp32
-// values into one register (bytes 2,3 of the second source, then of the first).
-__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-__device__ __forceinline__ void split_p8(const float p[8], bf16x8_t& hi, bf16x8_t& lo) {
-    float r[8];
+// 8 probabilities as one bf16 MFMA operand, rounded to nearest even (a pair
+// per v_cvt_pk_bf16_f32).  Each p is in (0, 2^8], so its relative rounding
+// error is at most 2^-9 and the output moves by at most 2^-9 of the spread of
+// the values it averages.
+__device__ __forceinline__ bf16x8_t to_bf16x8(const float p[8]) {
+    bf16x8_t r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = p[i] - __uint_as_float(__float_as_uint(p[i]) & 0xFFFF0000u);
-    hi = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_hi16(p[0], p[1]), pack_hi16(p[2], p[3]), pack_hi16(p[4], p[5]),
-                                              pack_hi16(p[6], p[7])});
-    lo = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_hi16(r[0], r[1]), pack_hi16(r[2], r[3]), pack_hi16(r[4], r[5]),
-                                              pack_hi16(r[6], r[7])});
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(p[i]);
+    return r;
 }
 
-// Staging registers for one iteration: thread t owns chunk t of each of the 4
-// blocks, for K (row t/16, 8 elements at (t%16)*8) and for V^T (d row t/2,
-// tokens (t%2)*8..+7).
+// Staging registers for one iteration: thread t owns 16 bytes of each of the
+// iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V^T tiles
+// (d row t/2, tokens (t%2)*8..+7); fp8 codes are converted to bf16 on load.
+// The tile addresses are uniform (one per block) and the thread's offset
+// inside a tile is fixed, so a load costs no vector arithmetic.
 template <int KV>
 struct Stage {
-    u32x4_t k[4], v[4];  // bf16 values (fp8 converted on load)
-    // valid[b]: tokens of block b at or past it are unwritten (only the row's
-    // last block is partial); their V is zeroed, since 0 * NaN is NaN.
-    __device__ __forceinline__ void load(const void* kp, const void* vp, const int64_t blk[4], const int valid[4],
-                                         int t) {
+    u32x4_t k[4], v[4];
+    __device__ __forceinline__ void load(const char* const kb[4], const char* const vb[4], uint32_t koff,
+                                         uint32_t voff) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if (blk[b] < 0) {
-                k[b] = u32x4_t{0, 0, 0, 0};
-                v[b] = u32x4_t{0, 0, 0, 0};
-                continue;
-            }
             if constexpr (KV == PKV_BF16) {
-                const uint16_t* kt = static_cast<const uint16_t*>(kp) + blk[b];
-                const uint16_t* vt = static_cast<const uint16_t*>(vp) + blk[b];
-                k[b] = ld<u32x4_t>(kt + (t >> 4) * kD + (t & 15) * 8);
-                v[b] = ld<u32x4_t>(vt + (t >> 1) * kBS + (t & 1) * 8);
+                k[b] = ld<u32x4_t>(kb[b] + koff);
+                v[b] = ld<u32x4_t>(vb[b] + voff);
             } else {
-                const uint8_t* kt = static_cast<const uint8_t*>(kp) + blk[b];
-                const uint8_t* vt = static_cast<const uint8_t*>(vp) + blk[b];
-                const u32x2_t kk = ld<u32x2_t>(kt + (t >> 4) * kD + (t & 15) * 8);
-                const u32x2_t vv = ld<u32x2_t>(vt + (t >> 1) * kBS + (t & 1) * 8);
+                const u32x2_t kk = ld<u32x2_t>(kb[b] + koff);
+                const u32x2_t vv = ld<u32x2_t>(vb[b] + voff);
                 const u32x2_t k0 = fp8x4_to_bf16x4(kk[0]), k1 = fp8x4_to_bf16x4(kk[1]);
                 const u32x2_t v0 = fp8x4_to_bf16x4(vv[0]), v1 = fp8x4_to_bf16x4(vv[1]);
                 k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
                 v[b] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
             }
-            if (valid[b] < kBS) {  // V^T chunk: tokens (t & 1) * 8 .. +7 of d row t / 2
-                const int tok0 = (t & 1) * 8;
-                uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
+        }
+    }
+    // Zero V^T of tokens at or past valid[b] (the row's partial last block and
+    // blocks past its end, which hold whatever the clamped load read; 0 * NaN
+    // is NaN).  Only the iteration that reaches the row's end calls this.
+    __device__ __forceinline__ void mask_tail(const int valid[4], int t) {
+        const int tok0 = (t & 1) * 8;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (tok0 + e >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-                v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
-            }
+        for (int b = 0; b < 4; ++b) {
+            uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (tok0 + e >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
     }
     __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs, int t) const {
@@ -131,10 +123,15 @@ struct Stage {
     }
 };
 
+// bf16 1.0 in both halves: the A operand of the "ones" tile whose product
+// with P^T is the row sum of P.
+constexpr uint32_t kOnes2 = 0x3F803F80u;
+
 template <int KV, int NT>
 __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
+    constexpr int kElt = (KV == PKV_BF16) ? 2 : 1;
 
     const int t = threadIdx.x;
     const int wave = t >> 6;
@@ -159,7 +156,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const int kend = row_ok ? P + jmax : 0;       // keys this tile needs
     const int n_iter = (kend + kKeys - 1) / kKeys;
     const int nblk_seq = (L + kBS - 1) / kBS;
-    const int64_t blk_stride = static_cast<int64_t>(p.hkv) * kTile;
+    const int64_t blk_bytes = static_cast<int64_t>(p.hkv) * kTile * kElt;
     const int32_t* trow = p.table + static_cast<int64_t>(row) * p.max_blocks;
 
     // this lane's query token (clamped for tile rows past the chunk's end)
@@ -189,56 +186,57 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         }
     }
 
-    float m[NT], l[NT];
-    f32x4_t acc[NT][8];
+    // acc[nt][0..7]: O^T d-tiles; acc[nt][8]: the row sum of P (ones tile)
+    float m[NT];
+    f32x4_t acc[NT][9];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m[nt] = -INFINITY;
-        l[nt] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[nt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 9; ++i) acc[nt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnes2, kOnes2, kOnes2, kOnes2});
 
-    const int koff = kvh * kTile;
-    const void* kp = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(koff) * (KV == PKV_BF16 ? 2 : 1);
-    const void* vp = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(koff) * (KV == PKV_BF16 ? 2 : 1);
+    const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
+    const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
+    const uint32_t koff = static_cast<uint32_t>(((t >> 4) * kD + (t & 15) * 8) * kElt);
+    const uint32_t voff = static_cast<uint32_t>(((t >> 1) * kBS + (t & 1) * 8) * kElt);
 
+    // Tile addresses of iteration it's 4 blocks (uniform).  Blocks past the
+    // row's end read its last block (their V is zeroed by mask_tail, their
+    // keys are masked); a block id outside the pool reads block 0 and makes
+    // the output NaN.
     bool bad = false;
-    auto block_offsets = [&](int it, int64_t blk[4], int valid[4]) {
+    auto stage_load = [&](Stage<KV>& sr, int it) {
+        const char* kb[4];
+        const char* vb[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int lb = it * 4 + b;
-            int32_t id = -1;
-            if (lb < nblk_seq) id = trow[lb];
-            if (lb < nblk_seq && (id < 0 || id >= p.num_blocks)) {
-                bad = true;
-                id = -1;
+            const int lb = min(it * 4 + b, nblk_seq - 1);
+            int32_t id = lb >= 0 ? trow[lb] : 0;
+            if (id < 0 || id >= p.num_blocks) {
+                bad = bad || lb >= 0;
+                id = 0;
             }
-            blk[b] = id < 0 ? -1 : static_cast<int64_t>(id) * blk_stride;
-            valid[b] = min(kBS, max(0, L - lb * kBS));
+            kb[b] = kpool + id * blk_bytes;
+            vb[b] = vpool + id * blk_bytes;
         }
+        sr.load(kb, vb, koff, voff);
+    };
+    auto stage_store = [&](Stage<KV>& sr, int it, int buf) {
+        if ((it + 1) * kKeys > L) {  // the iteration that reaches the row's end
+            int valid[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) valid[b] = min(kBS, max(0, L - (it * 4 + b) * kBS));
+            sr.mask_tail(valid, t);
+        }
+        sr.store(ks[buf], vs[buf], t);
     };
 
-    Stage<KV> sreg;
-    if (n_iter > 0) {
-        int64_t blk[4];
-        int valid[4];
-        block_offsets(0, blk, valid);
-        sreg.load(kp, vp, blk, valid, t);
-        sreg.store(ks[0], vs[0], t);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < n_iter; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < n_iter) {
-            int64_t blk[4];
-            int valid[4];
-            block_offsets(it + 1, blk, valid);
-            sreg.load(kp, vp, blk, valid, t);
-        }
-        const uint16_t* kc = ks[cur];
-        const uint16_t* vc = vs[cur];
+    // one iteration over the 64 keys staged in LDS buffer buf
+    auto compute = [&](int it, int buf) {
+        const uint16_t* kc = ks[buf];
+        const uint16_t* vc = vs[buf];
         const int kbase = it * kKeys;
         // S^T tiles: s[nt][b] holds keys kbase + 16 b + 4 g + i for token row r
         f32x4_t s[NT][4];
@@ -261,7 +259,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         // a query's position only in the iterations that reach the diagonal,
         // so only those take the masked path (a uniform branch).
         const bool need_mask = kbase + kKeys - 1 > P + j0;
-        bf16x8_t phi[NT][2], plo[NT][2];
+        bf16x8_t pb[NT][2];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             float x[16];
@@ -287,26 +285,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
                 mb = fmaxf(mb, __shfl_xor(mb, 32));
                 const float mn = fmaxf(m[nt], mb);
                 const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
-                l[nt] *= alpha;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[nt][i] *= alpha;
+                for (int i = 0; i < 9; ++i) acc[nt][i] *= alpha;
                 m[nt] = mn;
             }
             const float neg_m = -m[nt];
             float pr[16];
-            float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale, neg_m));
-                sum += pr[i];
-            }
-            l[nt] += sum;
+            for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale, neg_m));
             // k-step h covers blocks 2h, 2h+1: this lane's 8 keys are
             // (block 2h: 4g..4g+3, block 2h+1: 4g..4g+3)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) split_p8(pr + 8 * h, phi[nt][h], plo[nt][h]);
+            for (int h = 0; h < 2; ++h) pb[nt][h] = to_bf16x8(pr + 8 * h);
         }
-        // O^T += V^T . P^T
+        // O^T += V^T . P^T, and the row sum of P through the ones tile
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -317,13 +309,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
                 const u32x2_t a1 = ld<u32x2_t>(v1);
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[nt][h], acc[nt][mt], 0, 0, 0);
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[nt][h], acc[nt][mt], 0, 0, 0);
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][h], acc[nt][mt], 0, 0, 0);
             }
         }
-        if (it + 1 < n_iter) sreg.store(ks[cur ^ 1], vs[cur ^ 1], t);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nt][h], acc[nt][8], 0, 0, 0);
+    };
+
+    // One register stage and two LDS buffers: the loads for iteration it + 1
+    // are issued before iteration it is computed and stored to the other LDS
+    // buffer after it.  The loads are unconditional (clamped iteration), so no
+    // branch sits between a load and its use.
+    Stage<KV> sreg;
+    const int last = max(n_iter - 1, 0);
+    stage_load(sreg, 0);
+    if (n_iter > 0) stage_store(sreg, 0, 0);
+    __syncthreads();
+    for (int it = 0; it < n_iter; ++it) {
+        const int cur = it & 1;
+        stage_load(sreg, min(it + 1, last));
+        compute(it, cur);
+        if (it + 1 < n_iter) stage_store(sreg, it + 1, cur ^ 1);
         __syncthreads();
     }
 
@@ -331,11 +341,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const bool tok_ok = j0 + r < C;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        float lt = l[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
         if (!head_ok[nt] || !tok_ok) continue;
-        const float inv = bad ? __builtin_nanf("") : vscale / lt;
+        const float inv = bad ? __builtin_nanf("") : vscale / acc[nt][8][0];
         const int hh = wave * NT + nt;
         uint16_t* op = static_cast<uint16_t*>(p.out) +
                        (static_cast<int64_t>(qbeg + j0 + r) * p.hq + kvh * p.group + hh) * kD;
