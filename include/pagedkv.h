@@ -150,9 +150,12 @@ int block_table_build(const pkv_pool* pool, const int32_t* seqs, int32_t n, int3
  *   k_pool: [num_layers][num_blocks][num_kv_heads][16 tokens][head_dim]
  *   v_pool: [num_layers][num_blocks][num_kv_heads][head_dim][16 tokens]
  * (V is stored token-minor inside a block so that the P.V contraction over
- * tokens reads contiguous memory.)  Elements are kv_dtype.  For fp8, stored
- * value = e4m3(code) * scale with one fp32 scale per (layer, kv head) for K
- * (k_scale [num_layers][num_kv_heads]) and for V (v_scale); NULL otherwise. */
+ * tokens reads contiguous memory.)  fp8 V tiles (16 x 128 codes, 2 KiB) keep
+ * (d, token) at byte (token / 4) * 512 + (d % 16) * 32 + (d / 16) * 4 +
+ * token % 4, so the decode kernel reads them with 16-byte loads.
+ * Elements are kv_dtype.  For fp8, stored value = e4m3(code) * scale with
+ * one fp32 scale per (layer, kv head) for K (k_scale [num_layers]
+ * [num_kv_heads]) and for V (v_scale); NULL otherwise. */
 typedef struct {
     int32_t kv_dtype;     /* pkv_dtype */
     int32_t num_layers;
@@ -189,7 +192,8 @@ typedef struct {
     /* tuning and scratch: */
     int32_t decode_parts;        /* decode: the blocks of each kv head are divided evenly among this
                                     many wavefronts (<= 4096, and at most one per 8 blocks of the
-                                    head's work); 0 = auto (8 per compute unit in all) */
+                                    head's work); 0 = auto (8 per compute unit in all, 12 for an
+                                    fp8 cache) */
     void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that

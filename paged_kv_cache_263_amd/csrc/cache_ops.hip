@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
         const int64_t src = static_cast<int64_t>(i) * count + e;
         const int64_t tile = (static_cast<int64_t>(blk) * p.hkv + h) * kTile;
         const int64_t kdst = tile + o * kD + d;   // K tile [16][128]
-        const int64_t vdst = tile + d * kBS + o;  // V tile [128][16]
+        const int64_t vdst = tile + d * kBS + o;  // V tile [128][16] (fp8: see fp8_v_offset)
         if constexpr (KV == PKV_F32) {
             static_cast<float*>(p.k_pool)[kdst] = static_cast<const float*>(p.k_new)[src];
             static_cast<float*>(p.v_pool)[vdst] = static_cast<const float*>(p.v_new)[src];
@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
             const float xk = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.k_new)[src]) << 16);
             const float xv = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.v_new)[src]) << 16);
             static_cast<uint8_t*>(p.k_pool)[kdst] = static_cast<uint8_t>(e4m3_code_rne(xk / p.k_scale[h]));
-            static_cast<uint8_t*>(p.v_pool)[vdst] = static_cast<uint8_t>(e4m3_code_rne(xv / p.v_scale[h]));
+            static_cast<uint8_t*>(p.v_pool)[tile + fp8_v_offset(d, o)] =
+                static_cast<uint8_t>(e4m3_code_rne(xv / p.v_scale[h]));
         }
     }
 }

@@ -158,33 +158,43 @@ struct Tile<PKV_BF16> {
     }
 };
 
+// fp8 tiles are read with 16-byte loads (narrower loads cap the read rate
+// well below the HBM rate).  K: lane (r, g) reads codes 32 g .. 32 g + 31 of
+// token row r, and matrix step ks takes codes 32 g + 8 ks .. +7; the query
+// operand uses the same order of d (a permutation of the contraction index,
+// so the scores are unchanged).  V: the tile layout of fp8_v_offset puts the
+// lane's 8 words (tokens 4g..4g+3 of d rows 16 n + r) in 32 contiguous bytes.
 template <>
 struct Tile<PKV_FP8_E4M3> {
     using Elt = uint8_t;
     using Q = bf16x8_t[4];
-    u32x2_t k[4];   // 8 codes: K[tok r][32 ks + 8 g .. +7]
-    uint32_t v[8];  // 4 codes: V^T[16 n + r][4 g .. 4 g + 3]
+    u32x4_t k[2];  // codes 32 g .. 32 g + 31 of token row r
+    u32x4_t v[2];  // word n: tokens 4g..4g+3 of d row 16 n + r
     static __device__ __forceinline__ void load_q(Q& q, const void* qp, bool ok, int g) {
-        Tile<PKV_BF16>::load_q(q, qp, ok, g);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4_t x = ok ? ld<u32x4_t>(static_cast<const uint16_t*>(qp) + 32 * g + 8 * ks) : u32x4_t{0, 0, 0, 0};
+            q[ks] = __builtin_bit_cast(bf16x8_t, x);
+        }
     }
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) k[ks] = ld<u32x2_t>(kt + r * kD + 32 * ks + 8 * g);
+        for (int s = 0; s < 2; ++s) k[s] = ld<u32x4_t>(kt + r * kD + 32 * g + 16 * s);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) v[n] = ld<uint32_t>(vt + (16 * n + r) * kBS + 4 * g);
+        for (int s = 0; s < 2; ++s) v[s] = ld<u32x4_t>(vt + g * 512 + r * 32 + 16 * s);
     }
     __device__ __forceinline__ void mask_v(const bool keep[4]) {
         const uint32_t m = (keep[0] ? 0xFFu : 0u) | (keep[1] ? 0xFF00u : 0u) | (keep[2] ? 0xFF0000u : 0u) |
                            (keep[3] ? 0xFF000000u : 0u);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) v[n] &= m;
+        for (int s = 0; s < 2; ++s) v[s] &= u32x4_t{m, m, m, m};
     }
     __device__ __forceinline__ f32x4_t scores(const Q& q) const {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const u32x2_t a = fp8x4_to_bf16x4(k[ks][0]);
-            const u32x2_t b = fp8x4_to_bf16x4(k[ks][1]);
+            const u32x2_t a = fp8x4_to_bf16x4(k[ks >> 1][2 * (ks & 1)]);
+            const u32x2_t b = fp8x4_to_bf16x4(k[ks >> 1][2 * (ks & 1) + 1]);
             const u32x4_t kb = {a[0], a[1], b[0], b[1]};
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), q[ks], s, 0, 0, 0);
         }
@@ -195,7 +205,7 @@ struct Tile<PKV_FP8_E4M3> {
         split_p(p, hi, lo);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-            const i16x4_t a = __builtin_bit_cast(i16x4_t, fp8x4_to_bf16x4(v[n]));
+            const i16x4_t a = __builtin_bit_cast(i16x4_t, fp8x4_to_bf16x4(v[n >> 2][n & 3]));
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[n], 0, 0, 0);
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[n], 0, 0, 0);
         }
@@ -528,13 +538,15 @@ int decode_pipeline_depth() {
 }
 
 // Wavefronts per kv head: PKV_DECODE_WAVES_PER_CU wavefronts per compute
-// unit in total (default 8), shared among the kv heads.
-int decode_parts_auto(int hkv) {
-    static const int per_cu = [] {
+// unit in total (default 8; 12 for an fp8 cache, whose blocks carry half the
+// bytes for the same instruction count), shared among the kv heads.
+int decode_parts_auto(int hkv, int kv_dtype) {
+    static const int env = [] {
         const char* e = std::getenv("PKV_DECODE_WAVES_PER_CU");
-        const int v = e ? std::atoi(e) : 8;
-        return v < 1 ? 1 : (v > 32 ? 32 : v);
+        const int v = e ? std::atoi(e) : 0;
+        return v < 0 ? 0 : (v > 32 ? 32 : v);
     }();
+    const int per_cu = env > 0 ? env : (kv_dtype == PKV_FP8_E4M3 ? 12 : 8);
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -549,7 +561,7 @@ int decode_parts_auto(int hkv) {
 
 int32_t decode_parts(const pkv_cache* c, const pkv_attn_args* a) {
     if (a->decode_parts > 0) return a->decode_parts < kMaxParts ? a->decode_parts : kMaxParts;
-    return decode_parts_auto(c->num_kv_heads);
+    return decode_parts_auto(c->num_kv_heads, c->kv_dtype);
 }
 
 size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {

@@ -40,12 +40,23 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 // fp32 exactly (checked on all 256 codes); an E4M3 value has at most four
 // significant bits, so the fp32 result's low 16 bits are zero and its high
 // half is the bf16 encoding of the same value.
+// The two high halves are packed with one v_perm_b32 (bytes 2, 3 of the
+// first value, then of the second).
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
     const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-    return u32x2_t{(__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u),
-                   (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u)};
+    return u32x2_t{__builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u),
+                   __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u)};
+}
+
+// Byte offset of (d row, token) inside one fp8 V tile (2 KiB): tokens in
+// groups of 4, then d % 16, then d / 16, then the token within its group.
+// Lane (r, g) of the decode kernel then finds the 8 words it feeds to the
+// matrix cores - tokens 4g..4g+3 of d rows 16 n + r, n = 0..7 - in 32
+// contiguous bytes at g * 512 + r * 32, read as two 16-byte loads.
+__device__ __forceinline__ int fp8_v_offset(int d, int tok) {
+    return (tok >> 2) * 512 + (d & 15) * 32 + (d >> 4) * 4 + (tok & 3);
 }
 
 // fp32 -> E4M3 code: nearest, ties to even mantissa, |x| >= 448 saturates to

@@ -81,8 +81,10 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const float p[8]) {
 template <int KV>
 struct Stage {
     u32x4_t k[4], v[4];
+    // voff: this thread's V^T piece (bf16); fp8 tiles keep it as two 4-byte
+    // words at voff and voff1 (fp8_v_offset)
     __device__ __forceinline__ void load(const char* const kb[4], const char* const vb[4], uint32_t koff,
-                                         uint32_t voff) {
+                                         uint32_t voff, uint32_t voff1) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if constexpr (KV == PKV_BF16) {
@@ -90,7 +92,7 @@ struct Stage {
                 v[b] = ld<u32x4_t>(vb[b] + voff);
             } else {
                 const u32x2_t kk = ld<u32x2_t>(kb[b] + koff);
-                const u32x2_t vv = ld<u32x2_t>(vb[b] + voff);
+                const u32x2_t vv = {ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1)};
                 const u32x2_t k0 = fp8x4_to_bf16x4(kk[0]), k1 = fp8x4_to_bf16x4(kk[1]);
                 const u32x2_t v0 = fp8x4_to_bf16x4(vv[0]), v1 = fp8x4_to_bf16x4(vv[1]);
                 k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
@@ -200,7 +202,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const uint32_t koff = static_cast<uint32_t>(((t >> 4) * kD + (t & 15) * 8) * kElt);
-    const uint32_t voff = static_cast<uint32_t>(((t >> 1) * kBS + (t & 1) * 8) * kElt);
+    const uint32_t voff = static_cast<uint32_t>(
+        KV == PKV_BF16 ? ((t >> 1) * kBS + (t & 1) * 8) * kElt : fp8_v_offset(t >> 1, (t & 1) * 8));
+    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : fp8_v_offset(t >> 1, (t & 1) * 8 + 4));
 
     // Tile addresses of iteration it's 4 blocks (uniform).  Blocks past the
     // row's end read its last block (their V is zeroed by mask_tail, their
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
             kb[b] = kpool + id * blk_bytes;
             vb[b] = vpool + id * blk_bytes;
         }
-        sr.load(kb, vb, koff, voff);
+        sr.load(kb, vb, koff, voff, voff1);
     };
     auto stage_store = [&](Stage<KV>& sr, int it, int buf) {
         if ((it + 1) * kKeys > L) {  // the iteration that reaches the row's end

@@ -92,7 +92,10 @@ def test_fp8_codes_bit_exact():
     hip = HipSide(w)
     lens, starts = W.replay_lengths(w)
     kp = hip.cache.k_pool[0].cpu().numpy()  # [NB, hkv, 16, 128]
-    vp = hip.cache.v_pool[0].cpu().numpy()  # [NB, hkv, 128, 16]
+    # fp8 V tiles (2 KiB per block and kv head): (d, token) at byte
+    # (token // 4) * 512 + (d % 16) * 32 + (d // 16) * 4 + token % 4
+    vp = hip.cache.v_pool[0].cpu().numpy().reshape(w.num_blocks, w.hkv, 2048)
+    dd = np.arange(128)
     for op in w.script:
         if op.kind != "append":
             continue
@@ -102,7 +105,8 @@ def test_fp8_codes_bit_exact():
         blk, off = row[t // 16], t % 16
         for j in range(w.hkv):
             gk = kp[blk, j, off, :]
-            gv = vp[blk, j, :, off]
+            vidx = (off[:, None] // 4) * 512 + (dd[None, :] % 16) * 32 + (dd[None, :] // 16) * 4 + off[:, None] % 4
+            gv = vp[blk[:, None], j, vidx]
             ok = OF.quantise_scaled(k[:, j].float().cpu().numpy(), w.k_scale[j])
             ov = OF.quantise_scaled(v[:, j].float().cpu().numpy(), w.v_scale[j])
             assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
