@@ -6,12 +6,13 @@ One step is one decode step of the whole hot path for a batch of sequences
 whose K/V already sit in the paged cache in HBM:
   1. host allocator: one new token for every sequence (a new block every 16
      tokens, copy-on-write if the tail block is shared), slots returned;
-  2. one host-to-device copy of the slots and positions;
-  3. cache write: the new tokens' K/V to their slots, device block table and
-     lengths kept up to date in the same kernel;
-  4. paged decode: a plan kernel (prefix sum of blocks per row), the decode
-     kernel (the blocks of all rows divided evenly among the wavefronts of each
-     kv head), and the merge kernel for rows cut between wavefronts.
+  2. cache write: the new tokens' K/V to their slots, device block table and
+     lengths kept up to date in the same kernel, which reads the slots and
+     positions straight from the pinned host memory the allocator wrote;
+  3. paged decode: the decode kernel (the blocks of all rows divided evenly
+     among the wavefronts of each kv head, each wavefront taking the prefix
+     sum of blocks per row itself), and the merge kernel for rows cut between
+     wavefronts.
 ``value`` is the KV bytes every step attends (sum of lengths x kv heads x 128
 x 2 x element bytes) divided by the measured step time.  The line also
 carries the roofline of the dominant kernel (the decode kernel, timed
@@ -38,6 +39,56 @@ import torch
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "chunked")
+
+
+class TimingEvents:
+    """n x k hipEvents for timing kernels on one stream.  They are created with
+    hipEventDisableSystemFence: a default event's record also writes back and
+    invalidates the caches at system scope, which holds the next kernel back by
+    several microseconds; nothing waits on these events, they only carry
+    timestamps."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int, k: int):
+        import ctypes
+
+        import paged_kv_cache_263_amd as pk
+
+        vp = ctypes.c_void_p
+        self._create = pk._hip_fn("hipEventCreateWithFlags", ctypes.c_int, [ctypes.POINTER(vp), ctypes.c_uint])
+        self._record = pk._hip_fn("hipEventRecord", ctypes.c_int, [vp, vp])
+        self._elapsed = pk._hip_fn("hipEventElapsedTime", ctypes.c_int, [ctypes.POINTER(ctypes.c_float), vp, vp])
+        self._destroy = pk._hip_fn("hipEventDestroy", ctypes.c_int, [vp])
+        self.ev = []
+        for _ in range(n):
+            row = []
+            for _ in range(k):
+                e = vp()
+                if self._create(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                row.append(e.value)
+            self.ev.append(row)
+
+    def handles(self, i: int, idx=None):
+        return [self.ev[i][j] for j in (idx if idx is not None else range(len(self.ev[i])))]
+
+    def record(self, i: int, j: int, stream) -> None:
+        if self._record(self.ev[i][j], stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i: int, a: int, b: int) -> float:
+        import ctypes
+
+        out = ctypes.c_float()
+        if self._elapsed(ctypes.byref(out), self.ev[i][a], self.ev[i][b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def __del__(self):
+        for row in getattr(self, "ev", []):
+            for e in row:
+                self._destroy(e)
 
 
 def parse():
@@ -106,11 +157,7 @@ def run_chunked(args, w, device):
     cu_q = torch.tensor(cu, dtype=torch.int32, device=device)
     out = torch.empty_like(q)
     total = args.warmup + args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
-    stream = torch.cuda.current_stream()
-    for row in ev:
-        for e in row:
-            e.record(stream)
+    ev = TimingEvents(total, 4)
     mdl = max(lens[:nd])
     a = pk._args(cache, q, out, table, klens, max(lens), 0, args.decode_parts, None, cu_q=cu_q, num_decode=nd,
                  max_decode_kv_len=mdl, max_q_len=max(w.q_lens), total_q=q.shape[0])
@@ -120,7 +167,7 @@ def run_chunked(args, w, device):
     def step(i):
         pk.paged_attn_prefill_chunk(cache, q, cu_q, table, klens, max(lens), nd, max(w.q_lens), out=out,
                                     max_decode_kv_len=mdl, decode_parts=args.decode_parts, workspace=ws,
-                                    events=[e.cuda_event for e in ev[i]])
+                                    events=ev.handles(i))
 
     for i in range(args.warmup):
         step(i)
@@ -131,8 +178,8 @@ def run_chunked(args, w, device):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     timed = range(args.warmup, total)
-    dec_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in timed]))  # decode + merge
-    pre_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in timed]))
+    dec_ms = float(np.mean([ev.ms(i, 0, 2) for i in timed]))  # decode + merge
+    pre_ms = float(np.mean([ev.ms(i, 2, 3) for i in timed]))
     C = max(w.q_lens)
     P = lens[-1] - C
     flops = 4.0 * w.d * w.hq * (C * P + C * (C + 1) / 2)
@@ -403,17 +450,16 @@ def main():
     k_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
     v_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
     d_rows = torch.arange(B, dtype=torch.int32, device=device)
-    h_io = torch.empty((total, 2, B), dtype=torch.int32).pin_memory()  # slots, positions per step
-    d_io = torch.empty((2, B), dtype=torch.int32, device=device)
+    # slots and positions of every step, in pinned host memory that the cache
+    # write kernel reads directly (one row per step, so no step overwrites
+    # values an earlier, still queued step has yet to read)
+    h_io = torch.empty((total, 2, B), dtype=torch.int32).pin_memory()
     ones = [1] * B
     # workspace sized for the longest row the run reaches
     a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.decode_parts, None)
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
-    for row in ev:
-        for e in row:
-            e.record(stream)  # creates the underlying hipEvent
+    ev = TimingEvents(total, 4)
     torch.cuda.synchronize()
 
     kv_bytes_step = []
@@ -427,12 +473,15 @@ def main():
             copies_total += len(copies)
         h_io[i, 1].copy_(torch.from_numpy(lens.astype(np.int32)))  # position of the new token
         lens[:] += 1
-        d_io.copy_(h_io[i], non_blocking=True)
-        ev[i][0].record(stream)
-        pk.kv_cache_write(cache, k_new[i], v_new[i], d_io[0], rows=d_rows, positions=d_io[1],
+        # Timed steps carry only the two events around the decode kernel (its
+        # roofline); warmup steps also time the cache write and the merge.
+        breakdown = i < args.warmup
+        if breakdown:
+            ev.record(i, 0, stream)
+        pk.kv_cache_write(cache, k_new[i], v_new[i], h_io[i, 0], rows=d_rows, positions=h_io[i, 1],
                           block_table=d_table, kv_lens=d_lens)
         pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, decode_parts=args.decode_parts,
-                             workspace=ws, events=[ev[i][1].cuda_event, ev[i][2].cuda_event, ev[i][3].cuda_event])
+                             workspace=ws, events=ev.handles(i, (1, 2, 3) if breakdown else (1, 2)))
         kv_bytes_step.append(int(lens.sum()) * w.hkv * w.d * 2 * elt_bytes(w))
 
     for i in range(args.warmup):
@@ -448,9 +497,14 @@ def main():
     dt = time.perf_counter() - t0
 
     timed = range(args.warmup, total)
-    split_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in timed]  # decode kernel
-    merge_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in timed]
-    write_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]  # cache write + decode plan
+    split_ms = [ev.ms(i, 1, 2) for i in timed]  # decode kernel
+    late_warmup = range(max(0, args.warmup - 5), args.warmup)
+    merge_ms = [ev.ms(i, 2, 3) for i in late_warmup]
+    write_ms = [ev.ms(i, 0, 1) for i in late_warmup]  # cache write (+ plan kernel, if any)
+
+    def us(v):
+        return round(float(np.mean(v)) * 1e3, 2) if v else None
+
     bytes_timed = kv_bytes_step[args.warmup:]
     ms_per_step = dt * 1e3 / args.steps
     value = sum(bytes_timed) / dt / 1e9
@@ -476,9 +530,8 @@ def main():
                    "pool_blocks": w.num_blocks, "decode_parts": args.decode_parts or "auto",
                    "placement": args.placement},
         "seq_tokens_per_s": round(tokens_per_s, 1),
-        "kernels_us": {"decode": round(float(np.mean(split_ms)) * 1e3, 2),
-                       "decode_merge": round(float(np.mean(merge_ms)) * 1e3, 2),
-                       "cache_write_and_plan": round(float(np.mean(write_ms)) * 1e3, 2)},
+        "kernels_us": {"decode": us(split_ms), "decode_merge_warmup": us(merge_ms),
+                       "cache_write_warmup": us(write_ms)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if w.name == "llama8b" and not args.decode_parts else None,

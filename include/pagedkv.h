@@ -197,10 +197,10 @@ typedef struct {
     void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
-     * the call records on its stream: [0] after the decode plan kernel (just
-     * before the decode kernel), [1] after the decode kernel, [2] after the
-     * decode merge kernel, [3] after the prefill kernel.  The caller owns the
-     * events. */
+     * the call records on its stream: [0] just before the decode kernel (after
+     * the plan kernel that batches of more than 1024 rows need), [1] after the
+     * decode kernel, [2] after the decode merge kernel, [3] after the prefill
+     * kernel.  The caller owns the events. */
     void* events[4];
 } pkv_attn_args;
 
@@ -234,7 +234,10 @@ int paged_attn_prefill_chunk(const pkv_cache* cache, const pkv_attn_args* args, 
  * code = e4m3 round-to-nearest-even of fp32(x / scale), saturating at +-448).
  *   k_new, v_new: device [n_tokens][num_kv_heads][head_dim] of val_dtype
  *                 (F32 for an F32 cache, BF16 for BF16 and FP8 caches)
- *   slots:        device [n_tokens], slot = block*16 + offset (from seq_append)
+ *   slots:        [n_tokens], slot = block*16 + offset (from seq_append)
+ * slots, rows and positions may be device memory or pinned host memory mapped
+ * for the device (hipHostMalloc); the kernel then reads them over the host
+ * link, and the host must not change them until the call has run.
  * A slot outside the pool is skipped (the kernel cannot report it).
  * Optional device block-table upkeep (pass NULL block_table to skip): token i
  * belongs to batch row rows[i] (0 <= rows[i] < num_rows; block_table is

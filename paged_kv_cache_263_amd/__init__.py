@@ -352,6 +352,30 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _hip_fn(name, res, args):
+    # the HIP runtime the library is linked against (looked up through the library's own handle)
+    fn = getattr(_lib, name)
+    fn.restype, fn.argtypes = res, args
+    return fn
+
+
+def _dev_ptr(t):
+    """Device address of a device tensor, or of a pinned host tensor (which the
+    kernels then read over the host link, with no staging copy)."""
+    if t is None:
+        return None
+    if t.is_cuda:
+        return ctypes.c_void_p(t.data_ptr())
+    if not t.is_pinned():
+        raise PagedKVError(-1, "a host tensor passed to a device call must be pinned")
+    dev = ctypes.c_void_p()
+    st = _hip_fn("hipHostGetDevicePointer", ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                            ctypes.c_uint])(ctypes.byref(dev), t.data_ptr(), 0)
+    if st != 0 or not dev.value:
+        raise PagedKVError(-5, f"hipHostGetDevicePointer failed ({st})")
+    return dev
+
+
 def _args(cache: KVCache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace,
           cu_q=None, num_decode=0, max_decode_kv_len=0, max_q_len=0, total_q=0) -> pkv_attn_args:
     if q.dtype not in _QDT:
@@ -442,7 +466,8 @@ def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_
 
 def kv_cache_write(cache: KVCache, k_new, v_new, slots, layer: int = 0, rows=None, positions=None,
                    block_table=None, kv_lens=None, stream=None) -> None:
-    """Write [n, Hkv, 128] K/V values to their slots (device int32 [n])."""
+    """Write [n, Hkv, 128] K/V values to their slots (int32 [n]).  slots, rows
+    and positions may be device tensors or pinned host tensors."""
     if k_new.dtype != cache.value_dtype or v_new.dtype != cache.value_dtype:
         raise PagedKVError(-4, f"values must be {cache.value_dtype}")
     for t in (k_new, v_new, slots):
@@ -459,7 +484,8 @@ def kv_cache_write(cache: KVCache, k_new, v_new, slots, layer: int = 0, rows=Non
     max_blocks = int(block_table.shape[1]) if block_table is not None else 0
     _check(_lib.kv_cache_write(ctypes.byref(cache.desc), layer, n,
                                PKV_F32 if cache.value_dtype == torch.float32 else PKV_BF16,
-                               _ptr(k_new), _ptr(v_new), _ptr(slots), _ptr(rows), _ptr(positions), num_rows,
+                               _ptr(k_new), _ptr(v_new), _dev_ptr(slots), _dev_ptr(rows), _dev_ptr(positions),
+                               num_rows,
                                _ptr(block_table), max_blocks, _ptr(kv_lens), _stream(stream)))
 
 

@@ -7,6 +7,8 @@
 // "Sharing, and what makes a prefix reusable"; [P3] item (g)).  The fp8 cache
 // stores one byte per element ([P2] "Quantising the cache"): code = E4M3
 // round-to-nearest-even of fp32(x / scale), saturating at +-448.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -28,43 +30,84 @@ struct WriteParams {
     int32_t n, hkv, num_blocks, num_rows, max_blocks;
 };
 
+// Four consecutive d of one head of one token: the values as read, and
+// their stores into the K tile ([16][128]) and the V tile ([128][16]; fp8:
+// fp8_v_offset).
+template <int KV>
+struct Quad {
+    using T = typename std::conditional<KV == PKV_F32, f32x4_t, u32x2_t>::type;  // 4 f32 or 4 bf16
+    T k, v;
+    __device__ __forceinline__ void load(const WriteParams& p, int64_t e) {  // e: element index, multiple of 4
+        if constexpr (KV == PKV_F32) {
+            k = ld<f32x4_t>(static_cast<const float*>(p.k_new) + e);
+            v = ld<f32x4_t>(static_cast<const float*>(p.v_new) + e);
+        } else {
+            k = ld<u32x2_t>(static_cast<const uint16_t*>(p.k_new) + e);
+            v = ld<u32x2_t>(static_cast<const uint16_t*>(p.v_new) + e);
+        }
+    }
+    __device__ __forceinline__ void store(const WriteParams& p, int64_t tile, int o, int h, int d) const {
+        if constexpr (KV == PKV_F32) {
+            float* kp = static_cast<float*>(p.k_pool) + tile;
+            float* vp = static_cast<float*>(p.v_pool) + tile;
+            st<f32x4_t>(kp + o * kD + d, k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vp[(d + j) * kBS + o] = v[j];
+        } else if constexpr (KV == PKV_BF16) {
+            uint16_t* kp = static_cast<uint16_t*>(p.k_pool) + tile;
+            uint16_t* vp = static_cast<uint16_t*>(p.v_pool) + tile;
+            st<u32x2_t>(kp + o * kD + d, k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vp[(d + j) * kBS + o] = static_cast<uint16_t>(v[j >> 1] >> (16 * (j & 1)));
+        } else {
+            uint8_t* kp = static_cast<uint8_t*>(p.k_pool) + tile;
+            uint8_t* vp = static_cast<uint8_t*>(p.v_pool) + tile;
+            const float ks = p.k_scale[h];
+            const float vs = p.v_scale[h];
+            uint32_t kc = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float xk = __uint_as_float((k[j >> 1] >> (16 * (j & 1))) << 16);
+                const float xv = __uint_as_float((v[j >> 1] >> (16 * (j & 1))) << 16);
+                kc |= e4m3_code_rne(xk / ks) << (8 * j);
+                vp[fp8_v_offset(d + j, o)] = static_cast<uint8_t>(e4m3_code_rne(xv / vs));
+            }
+            st<uint32_t>(kp + o * kD + d, kc);
+        }
+    }
+};
+
+// One workgroup per token, one thread per four consecutive d of one head.
+// Every load that depends on nothing else - slot, row and position (which
+// may sit in host memory) and the thread's first four values - is issued
+// before any is used, so the kernel waits for one round of loads.
 template <int KV>
 __global__ __launch_bounds__(256) void kv_write_kernel(const WriteParams p) {
     const int i = blockIdx.x;
+    const int t = threadIdx.x;
+    const int quads = p.hkv * (kD / 4);
+    const int64_t first = static_cast<int64_t>(i) * p.hkv * kD;
     const int slot = p.slots[i];
+    const bool upkeep = p.table != nullptr && t == 0;
+    const int row = upkeep ? p.rows[i] : 0;
+    const int pos = upkeep ? p.positions[i] : 0;
+    const int next_row = (upkeep && i + 1 < p.n) ? p.rows[i + 1] : -1;
+    Quad<KV> q0;
+    if (t < quads) q0.load(p, first + 4 * t);
     const bool slot_ok = slot >= 0 && slot < p.num_blocks * kBS;
-    if (threadIdx.x == 0 && p.table && slot_ok) {
-        const int row = p.rows[i];
-        const int pos = p.positions[i];
-        if (row >= 0 && row < p.num_rows && pos >= 0 && pos / kBS < p.max_blocks) {
-            p.table[static_cast<int64_t>(row) * p.max_blocks + pos / kBS] = slot / kBS;
-            if (i == p.n - 1 || p.rows[i + 1] != row) p.kv_lens[row] = pos + 1;
-        }
-    }
     if (!slot_ok) return;
+    if (upkeep && row >= 0 && row < p.num_rows && pos >= 0 && pos / kBS < p.max_blocks) {
+        p.table[static_cast<int64_t>(row) * p.max_blocks + pos / kBS] = slot / kBS;
+        if (next_row != row) p.kv_lens[row] = pos + 1;
+    }
     const int blk = slot / kBS;
     const int o = slot % kBS;
-    const int count = p.hkv * kD;
-    for (int e = threadIdx.x; e < count; e += blockDim.x) {
-        const int h = e / kD;
-        const int d = e % kD;
-        const int64_t src = static_cast<int64_t>(i) * count + e;
-        const int64_t tile = (static_cast<int64_t>(blk) * p.hkv + h) * kTile;
-        const int64_t kdst = tile + o * kD + d;   // K tile [16][128]
-        const int64_t vdst = tile + d * kBS + o;  // V tile [128][16] (fp8: see fp8_v_offset)
-        if constexpr (KV == PKV_F32) {
-            static_cast<float*>(p.k_pool)[kdst] = static_cast<const float*>(p.k_new)[src];
-            static_cast<float*>(p.v_pool)[vdst] = static_cast<const float*>(p.v_new)[src];
-        } else if constexpr (KV == PKV_BF16) {
-            static_cast<uint16_t*>(p.k_pool)[kdst] = static_cast<const uint16_t*>(p.k_new)[src];
-            static_cast<uint16_t*>(p.v_pool)[vdst] = static_cast<const uint16_t*>(p.v_new)[src];
-        } else {
-            const float xk = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.k_new)[src]) << 16);
-            const float xv = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.v_new)[src]) << 16);
-            static_cast<uint8_t*>(p.k_pool)[kdst] = static_cast<uint8_t>(e4m3_code_rne(xk / p.k_scale[h]));
-            static_cast<uint8_t*>(p.v_pool)[tile + fp8_v_offset(d, o)] =
-                static_cast<uint8_t>(e4m3_code_rne(xv / p.v_scale[h]));
-        }
+    for (int e = t; e < quads; e += blockDim.x) {
+        Quad<KV> qv = q0;
+        if (e != t) qv.load(p, first + 4 * e);
+        const int h = e / (kD / 4);
+        const int d = 4 * (e % (kD / 4));
+        qv.store(p, (static_cast<int64_t>(blk) * p.hkv + h) * kTile, o, h, d);
     }
 }
 

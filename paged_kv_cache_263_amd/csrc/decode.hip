@@ -31,8 +31,9 @@
 //
 // Work division.  Rows have very different lengths, so fixed-size chunks per
 // row leave some wavefronts long tails of work while others sit idle.  Here
-// a plan kernel turns the row lengths into a prefix sum of blocks per row;
-// for kv head h, wavefront i of Q takes blocks [floor(i U / Q), floor((i+1) U
+// the row lengths become a prefix sum of blocks per row (the plan: taken by
+// every wavefront itself for up to 1024 rows, else by a plan kernel); for kv
+// head h, wavefront i of Q takes blocks [floor(i U / Q), floor((i+1) U
 // / Q)) of the U blocks of all rows in row order, so every wavefront streams
 // the same number of blocks (within one).  A row entirely inside one range is
 // finished and written by that wavefront; a row cut by range boundaries is
@@ -306,6 +307,17 @@ struct Online {
     }
 };
 
+// Writes NaN over the whole output row b (lanes share the elements).
+template <int QT>
+__device__ __forceinline__ void nan_row(const DecodeParams& p, int b, int lane, int lanes) {
+    for (int e = lane; e < p.hq * kD; e += lanes) {
+        if constexpr (QT == PKV_F32)
+            static_cast<float*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = __builtin_nanf("");
+        else
+            static_cast<uint16_t*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = 0x7FC0u;
+    }
+}
+
 // Plan: prefix sum of blocks per row (invalid rows count 0 blocks and get NaN
 // output here).  One workgroup of 1024 threads, rows in chunks of 1024.
 template <int QT>
@@ -342,19 +354,12 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
         __syncthreads();
         if (t == 1023) carry_sh = v + add;
         __syncthreads();
-        if (invalid) {  // the whole row becomes NaN
-            const float nan = __builtin_nanf("");
-            for (int e = 0; e < p.hq * kD; ++e) {
-                if constexpr (QT == PKV_F32)
-                    static_cast<float*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = nan;
-                else
-                    static_cast<uint16_t*>(p.out)[static_cast<int64_t>(b) * p.hq * kD + e] = 0x7FC0u;
-            }
-        }
+        if (invalid) nan_row<QT>(p, b, 0, 1);  // the whole row becomes NaN
     }
 }
 
-// Index of the row holding block position x: plan[b] <= x < plan[b+1].
+// Index of the row holding block position x: plan[b] <= x < plan[b+1]
+// (plan in LDS or in global memory).
 __device__ __forceinline__ int find_row(const int32_t* plan, int rows, int64_t x) {
     int lo = 0, hi = rows;  // invariant: plan[lo] <= x < plan[hi]
     while (hi - lo > 1) {
@@ -364,9 +369,59 @@ __device__ __forceinline__ int find_row(const int32_t* plan, int rows, int64_t x
     return lo;
 }
 
-template <int KV, int NBUF>
+// Batches of at most kLocalPlanRows rows skip the plan kernel: every
+// wavefront computes the prefix sum of blocks per row itself, into LDS (one
+// coalesced load of 64 row lengths and one wave scan per 64 rows), and
+// workgroup 0 also stores it for the merge kernel and writes the NaN output
+// of invalid rows.  This takes one short kernel and its
+// dependent global loads (a binary search through the global plan) off the
+// start of every wavefront.
+constexpr int kLocalPlanRows = 1024;
+
+template <int QT>
+__device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_sh, int lane) {
+    int carry = 0;
+#pragma unroll 1
+    for (int base = 0; base < p.rows; base += 64) {
+        const int b = base + lane;
+        int nb = 0;
+        bool invalid = false;
+        if (b < p.rows) {
+            const int L = p.kv_lens[b];
+            invalid = !row_valid(L, p);
+            nb = invalid ? 0 : (L + kBS - 1) / kBS;
+        }
+        int v = nb;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(v, off);
+            if (lane >= off) v += u;
+        }
+        if (b < p.rows) {
+            plan_sh[b + 1] = carry + v;
+            if (blockIdx.x == 0) p.plan[b + 1] = carry + v;
+        }
+        carry += __shfl(v, 63);
+        if (blockIdx.x == 0) {
+            uint64_t bad = __ballot(b < p.rows && invalid);
+            while (bad) {
+                const int k = __builtin_ctzll(bad);
+                bad &= bad - 1;
+                nan_row<QT>(p, base + k, lane, 64);
+            }
+        }
+    }
+    if (lane == 0) {
+        plan_sh[0] = 0;
+        if (blockIdx.x == 0) p.plan[0] = 0;
+    }
+    __syncthreads();
+}
+
+template <int KV, int NBUF, bool LOCAL_PLAN>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
+    __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
     using Elt = typename Tile<KV>::Elt;
     const int lane = threadIdx.x;
@@ -377,7 +432,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     // head's shared-prefix blocks in its own L2).
     const int kvh = blockIdx.x % p.hkv;
     const int wi = blockIdx.x / p.hkv;
-    const int64_t U = p.plan[p.rows];
+    if constexpr (LOCAL_PLAN) local_plan<QT>(p, plan_sh, lane);
+    const int32_t* plan = LOCAL_PLAN ? plan_sh : p.plan;
+    const int64_t U = plan[p.rows];
     const int Q = effective_parts(U, p.parts);
     if (wi >= Q || U <= 0) return;
     const int64_t u0 = range_start(U, wi, Q);
@@ -397,11 +454,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     const Elt* vpool = static_cast<const Elt*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile;
     const int64_t blk_stride = static_cast<int64_t>(p.hkv) * kTile;
 
-    int b = find_row(p.plan, p.rows, u0);
+    int b = find_row(plan, p.rows, u0);
     const int b_first = b;
     for (int64_t u = u0; u < u1; ++b) {
-        const int64_t rb0 = p.plan[b];
-        const int64_t rb1 = p.plan[b + 1];
+        const int64_t rb0 = plan[b];
+        const int64_t rb1 = plan[b + 1];
         if (rb1 <= u) continue;  // a row with no blocks
         const int L = p.kv_lens[b];
         const int j0 = static_cast<int>(u - rb0);
@@ -472,13 +529,15 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
 // Merge the pieces of one (row, query head) that was divided between
 // wavefronts: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
-// M = max_i m_i, in wavefront order.  The weights are computed once into LDS;
-// each lane (one per d) then sums the pieces.
+// M = max_i m_i, in wavefront order.  One lane per d.  The pieces are read
+// kMergeBatch at a time with every load of a batch issued together (indices
+// past the last piece repeat it and are left out of the sums), so a row cut
+// into at most kMergeBatch pieces costs one round of global loads after the
+// plan's.
 constexpr int kMaxParts = 4096;
+constexpr int kMergeBatch = 8;
 template <int QT>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p) {
-    __shared__ float wsh[kMaxParts];
-    __shared__ float red[2];
     const int64_t qrow = blockIdx.x;
     const int b = static_cast<int>(qrow / p.hq);
     const int hq = static_cast<int>(qrow % p.hq);
@@ -488,7 +547,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
     const int64_t U = p.plan[p.rows];
     const int64_t rb0 = p.plan[b];
     const int64_t rb1 = p.plan[b + 1];
-    if (rb1 <= rb0 || U <= 0) return;  // invalid row (NaN written by the plan kernel)
+    if (rb1 <= rb0 || U <= 0) return;  // invalid row (NaN written with the plan)
     const int Q = effective_parts(U, p.parts);
     // wavefronts whose ranges meet [rb0, rb1)
     int i0 = static_cast<int>(rb0 * Q / U);
@@ -499,25 +558,54 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
     while (i1 > 0 && range_start(U, i1, Q) > rb1 - 1) --i1;
     if (i0 == i1) return;  // written directly by the one wavefront
     const int n = i1 - i0 + 1;
-    auto slot = [&](int k) -> int64_t {
-        const int i = i0 + k;
-        const int side = range_start(U, i, Q) < rb0 ? 1 : 0;
-        return ((static_cast<int64_t>(kvh) * p.parts + i) * 2 + side) * p.group + hh;
-    };
-    float mx = -INFINITY;
-    for (int k = d; k < n; k += 128) mx = fmaxf(mx, p.ws_ml[2 * slot(k)]);
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((d & 63) == 0) red[d >> 6] = mx;
-    __syncthreads();
-    mx = fmaxf(red[0], red[1]);
-    for (int k = d; k < n; k += 128) wsh[k] = __builtin_amdgcn_exp2f(p.ws_ml[2 * slot(k)] - mx);
-    __syncthreads();
-    float num = 0.f, den = 0.f;
-    for (int k = 0; k < n; ++k) {
-        const int64_t sl = slot(k);
-        num += p.ws_acc[sl * kD + d] * wsh[k];
-        den += p.ws_ml[2 * sl + 1] * wsh[k];
+    // Piece k comes from wavefront i0 + k.  Only the first can have started
+    // its range in an earlier row (then this row is its second piece, side 1);
+    // every later one starts inside this row, so the row is its first piece.
+    const int side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
+    const int grp = p.group;
+    const int64_t base = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp + hh;
+    const float* __restrict__ ws_ml = p.ws_ml;
+    const float* __restrict__ ws_acc = p.ws_acc;
+    // piece k (clamped to the last piece) -> workspace slot
+#define PKV_MERGE_SLOT(k) (base + (2 * min((k), n - 1) + ((k) == 0 ? side0 : 0)) * grp)
+    float2 ml[kMergeBatch];
+    float acc[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+        const int64_t sl = PKV_MERGE_SLOT(j);
+        ml[j] = ld<float2>(ws_ml + 2 * sl);
+        acc[j] = ws_acc[sl * kD + d];
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, ml[j].x);  // repeats are real pieces
+    for (int k0 = kMergeBatch; k0 < n; k0 += kMergeBatch) {
+        float m[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) m[j] = ws_ml[2 * PKV_MERGE_SLOT(k0 + j)];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, m[j]);
+    }
+    float num = 0.f, den = 0.f;
+    for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+        if (k0 > 0) {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const int64_t sl = PKV_MERGE_SLOT(k0 + j);
+                ml[j] = ld<float2>(ws_ml + 2 * sl);
+                acc[j] = ws_acc[sl * kD + d];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (k0 + j < n) {
+                const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
+                num += acc[j] * w;
+                den += ml[j].y * w;
+            }
+        }
+    }
+#undef PKV_MERGE_SLOT
     const float o = num / den;
     if constexpr (QT == PKV_F32) {
         static_cast<float*>(p.out)[qrow * kD + d] = o;
@@ -555,6 +643,25 @@ int decode_parts_auto(int hkv, int kv_dtype) {
     }();
     const int parts = (cus * per_cu + hkv - 1) / hkv;
     return parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts);
+}
+
+template <bool LOCAL>
+void launch_decode_kernel(int kv_dtype, int depth, dim3 grid, hipStream_t stream, const DecodeParams& p) {
+    switch (kv_dtype) {
+        case PKV_F32:
+            hipLaunchKernelGGL((decode_kernel<PKV_F32, 2, LOCAL>), grid, dim3(64), 0, stream, p);
+            break;
+        case PKV_BF16:
+            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 2, LOCAL>), grid, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 3, LOCAL>), grid, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_kernel<PKV_BF16, 4, LOCAL>), grid, dim3(64), 0, stream, p);
+            break;
+        default:
+            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 2, LOCAL>), grid, dim3(64), 0, stream, p);
+            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 3, LOCAL>), grid, dim3(64), 0, stream, p);
+            else hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 4, LOCAL>), grid, dim3(64), 0, stream, p);
+            break;
+    }
 }
 
 }  // namespace
@@ -618,28 +725,20 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.scale_log2 = kLog2e / sqrtf(static_cast<float>(kD));
 
     const bool f32 = a->q_dtype == PKV_F32;
-    if (f32)
-        hipLaunchKernelGGL(decode_plan_kernel<PKV_F32>, dim3(1), dim3(1024), 0, stream, p);
-    else
-        hipLaunchKernelGGL(decode_plan_kernel<PKV_BF16>, dim3(1), dim3(1024), 0, stream, p);
+    const bool local = rows <= kLocalPlanRows;
+    if (!local) {
+        if (f32)
+            hipLaunchKernelGGL(decode_plan_kernel<PKV_F32>, dim3(1), dim3(1024), 0, stream, p);
+        else
+            hipLaunchKernelGGL(decode_plan_kernel<PKV_BF16>, dim3(1), dim3(1024), 0, stream, p);
+    }
     mark(0);
     const dim3 g1(static_cast<unsigned>(grid));
     const int depth = decode_pipeline_depth();
-    switch (c->kv_dtype) {
-        case PKV_F32:
-            hipLaunchKernelGGL((decode_kernel<PKV_F32, 2>), g1, dim3(64), 0, stream, p);
-            break;
-        case PKV_BF16:
-            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 2>), g1, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 3>), g1, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_kernel<PKV_BF16, 4>), g1, dim3(64), 0, stream, p);
-            break;
-        default:
-            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 2>), g1, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 3>), g1, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 4>), g1, dim3(64), 0, stream, p);
-            break;
-    }
+    if (local)
+        launch_decode_kernel<true>(c->kv_dtype, depth, g1, stream, p);
+    else
+        launch_decode_kernel<false>(c->kv_dtype, depth, g1, stream, p);
     mark(1);
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * a->num_q_heads));
     if (f32)

@@ -202,13 +202,40 @@ def test_invalid_rows_give_nan_and_others_stay_right():
     del good
 
 
-def test_device_table_upkeep_matches_host_tables():
-    """Decode steps that append one token per row and keep the device table
-    and lengths up to date inside the cache write end with the same table
-    the host allocator builds."""
+@pytest.mark.parametrize("rows", [1024, 1100])
+def test_many_rows_both_plan_paths(rows):
+    """Up to 1024 rows, every decode wavefront computes the prefix sum of
+    blocks per row itself; above that, a plan kernel does.  Both give the
+    oracle's result on sampled rows, and NaN on invalid rows (empty, negative,
+    or longer than the stated bound) wherever they sit in the batch."""
     import paged_kv_cache_263_amd as pk
 
-    case("device table upkeep")
+    rng = np.random.default_rng(rows)
+    w = W.custom(rng.integers(1, 97, rows).tolist(), 8, 2, "bf16", seed=91, variant="peaked")
+    case(f"many rows: {rows}")
+    hip = HipSide(w)
+    sample = sorted({0, 1, 62, 63, 64, 65, 511, 1022, 1023, rows - 1} | set(rng.integers(0, rows, 20).tolist()))
+    sample = [b for b in sample if b < rows]
+    check_decode(w, rows=sample, hip=hip)
+    lens = hip.kv_lens.clone()
+    bad = [3, 64, rows - 1]
+    lens[3] = 0
+    lens[64] = hip.max_kv_len + 1
+    lens[rows - 1] = -5
+    out = pk.paged_attn_decode(hip.cache, hip.q, hip.table, lens, hip.max_kv_len)
+    torch.cuda.synchronize()
+    orc = OracleSide(w)
+    for b in bad:
+        assert torch.isnan(out[b].float()).all(), f"row {b} not NaN"
+    for b in (0, 65, rows - 2):
+        compare(out[b].float().cpu().numpy(), orc.decode(b), TOL["bf16"], f"valid row {b}")
+
+
+def _append_steps(host_io):
+    """40 decode-style appends (one token per row) written with device table
+    upkeep; slots/positions from device tensors or from pinned host tensors."""
+    import paged_kv_cache_263_amd as pk
+
     w = W.custom([15, 16, 17, 100, 1], 8, 2, "bf16", seed=71, pool_factor=3.0)
     hip = HipSide(w)
     n = len(w.batch)
@@ -217,19 +244,48 @@ def test_device_table_upkeep_matches_host_tables():
     table[:, : hip.max_blocks] = hip.table
     lens = hip.kv_lens.clone()
     g = torch.Generator(device="cuda").manual_seed(3)
+    keep = []
     for step in range(40):
         slots, copies = pk.seq_append_batch(hip.pool, w.batch, [1] * n)
         assert not copies
         pos = [pk.seq_len(hip.pool, s) - 1 for s in w.batch]
         k = torch.randn((n, 2, 128), generator=g, device="cuda").bfloat16()
         v = torch.randn((n, 2, 128), generator=g, device="cuda").bfloat16()
-        pk.kv_cache_write(hip.cache, k, v, torch.tensor(slots, dtype=torch.int32, device="cuda"),
-                          rows=torch.arange(n, dtype=torch.int32, device="cuda"),
-                          positions=torch.tensor(pos, dtype=torch.int32, device="cuda"),
-                          block_table=table, kv_lens=lens)
-    ht, hl = pk.block_table_build(hip.pool, w.batch, mb)
+        if host_io:  # read by the kernel over the host link; alive until the sync below
+            st = torch.tensor(slots, dtype=torch.int32).pin_memory()
+            pt = torch.tensor(pos, dtype=torch.int32).pin_memory()
+            keep += [st, pt]
+        else:
+            st = torch.tensor(slots, dtype=torch.int32, device="cuda")
+            pt = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        pk.kv_cache_write(hip.cache, k, v, st, rows=torch.arange(n, dtype=torch.int32, device="cuda"),
+                          positions=pt, block_table=table, kv_lens=lens)
     torch.cuda.synchronize()
+    return w, hip, table, lens, mb
+
+
+def test_device_table_upkeep_matches_host_tables():
+    """Decode steps that append one token per row and keep the device table
+    and lengths up to date inside the cache write end with the same table
+    the host allocator builds."""
+    import paged_kv_cache_263_amd as pk
+
+    case("device table upkeep")
+    w, hip, table, lens, mb = _append_steps(False)
+    ht, hl = pk.block_table_build(hip.pool, w.batch, mb)
     assert torch.equal(table.cpu(), ht) and torch.equal(lens.cpu(), hl)
+
+
+def test_cache_write_reads_pinned_host_slots():
+    """Slots and positions passed in pinned host memory (read by the kernel
+    over the host link) give the same table, lengths and cache bytes as the
+    same values in device memory."""
+    case("cache write from pinned host slots")
+    _, dev, t_dev, l_dev, _ = _append_steps(False)
+    _, host, t_host, l_host, _ = _append_steps(True)
+    assert torch.equal(t_dev, t_host) and torch.equal(l_dev, l_host)
+    for a, b in zip((dev.cache.k_pool, dev.cache.v_pool), (host.cache.k_pool, host.cache.v_pool)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
 def test_second_layer():
