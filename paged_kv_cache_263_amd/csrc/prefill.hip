@@ -9,22 +9,26 @@
 // run on the matrix cores with shapes the hardware takes whole ([P1] "Kernel
 // engineering: the layer underneath everything else here" on tile shapes).
 //
-// Work decomposition: one workgroup (4 waves) per (chunk row, kv head, tile of
-// 16 query tokens); the G query heads of the kv head are split over the waves
-// (NT heads per wave), so each staged K/V tile serves 16 * G query rows.
-// Per iteration the workgroup gathers 64 keys (4 blocks, through the block
-// table) into LDS - K as [key][d] with rows padded to 136 elements, V as
-// [block][d][16 tokens] with rows padded to 20 elements, both to keep the
-// operand reads free of bank conflicts - double buffered, one barrier per
-// iteration.  Each wave then computes, per head tile (16 tokens of one head):
-//   S^T[64 keys x 16 tokens] = K . Q^T           (16 x mfma 16x16x32 bf16)
-//   O^T[128 x 16 tokens]    += V^T . P^T         (8 d-tiles x 2 key halves, P rounded to bf16)
-// with the running max / normaliser of the decode kernel (rescaled lazily,
-// only when a score passes the reference max by 2^8) and the causal mask
-// applied only where a key can pass a query's position.  For P.V the 32 keys
-// of one instruction are taken in the order the score tiles leave them in the
-// lanes (keys 4g..4g+3 of two consecutive blocks), and V is read in the same
-// order, so no lane exchange is needed between the two products.
+// Work decomposition: one workgroup (4 waves) per (chunk row, kv head, tile
+// of query rows).  A query row is one (token, query head) pair; the G heads of
+// one kv head share its K/V, so a tile holds 128 / G consecutive tokens with
+// all G heads each (128 rows), and wave w owns rows 32 w .. 32 w + 31 (row n
+// is token n / G, head n % G).  Per iteration the workgroup gathers 64 keys
+// (4 blocks, through the block table) into LDS - K as [key][d] with rows
+// padded to 136 elements (conflict-free operand reads), V as the cache's own
+// [d][16 tokens] tiles - double buffered, one barrier per iteration.  Each
+// wave then computes, on the 32x32x16 bf16 matrix instruction:
+//   S^T[64 keys x 32 rows] = K . Q^T        (2 key tiles x 8 steps over d)
+//   O^T[128 x 32 rows]    += V^T . P^T      (4 d tiles x 4 steps of 16 keys)
+// The lane holding a score column keeps that row's softmax state: running
+// max (rescaled lazily, only when a score passes it by 2^8) and normaliser.
+// The rows of K fed to the score product are permuted (bits 2 and 3 of the
+// key index swapped), so that the score registers come out holding, for each
+// 16-key step, exactly the 8 consecutive keys the P.V operand of that lane
+// needs: P goes from the score registers to the second product with no lane
+// exchange, and V is read in the cache's order.  P is rounded to bf16 once;
+// the normaliser sums the same rounded values (bf16 dot products with 1.0),
+// so the rounding largely cancels between numerator and denominator.
 // fp8 caches are converted to bf16 while staging (exact) with the per-head
 // scales folded into the score scale and the output.
 #include <cmath>
@@ -40,13 +44,14 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
 
 namespace {
 
-constexpr int kQTile = 16;             // query tokens per workgroup
+constexpr int kRows = 128;             // query rows per workgroup (4 waves x 32)
 constexpr int kKeys = 64;              // keys per iteration (4 blocks)
 constexpr int kKStride = kD + 8;       // padded K row (elements)
-constexpr int kVStride = kBS + 4;      // padded V^T row (elements)
-constexpr int kKStage = 4 * kBS * kKStride;   // elements of one K stage
-constexpr int kVStage = 4 * kD * kVStride;    // elements of one V stage
-constexpr float kLazy = 8.0f;                 // rescale threshold (log2 units)
+constexpr int kKStage = kKeys * kKStride;  // elements of one K stage
+constexpr int kVStage = 4 * kTile;         // elements of one V stage (4 tiles [128][16])
+constexpr float kLazy = 8.0f;              // rescale threshold (log2 units)
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct PrefillParams {
     const void* q;          // [total_q][hq][128] bf16
@@ -58,30 +63,19 @@ struct PrefillParams {
     const int32_t* table;   // [num_seqs][max_blocks]
     const int32_t* kv_lens; // [num_seqs]
     const int32_t* cu_q;    // [num_seqs + 1]
-    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q;
+    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
 };
 
-// 8 probabilities as one bf16 MFMA operand, rounded to nearest even (a pair
-// per v_cvt_pk_bf16_f32).  Each p is in (0, 2^8], so its relative rounding
-// error is at most 2^-9 and the output moves by at most 2^-9 of the spread of
-// the values it averages.
-__device__ __forceinline__ bf16x8_t to_bf16x8(const float p[8]) {
-    bf16x8_t r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(p[i]);
-    return r;
-}
-
 // Staging registers for one iteration: thread t owns 16 bytes of each of the
-// iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V^T tiles
+// iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V tiles
 // (d row t/2, tokens (t%2)*8..+7); fp8 codes are converted to bf16 on load.
 // The tile addresses are uniform (one per block) and the thread's offset
 // inside a tile is fixed, so a load costs no vector arithmetic.
 template <int KV>
 struct Stage {
     u32x4_t k[4], v[4];
-    // voff: this thread's V^T piece (bf16); fp8 tiles keep it as two 4-byte
+    // voff: this thread's V piece (bf16); fp8 tiles keep it as two 4-byte
     // words at voff and voff1 (fp8_v_offset)
     __device__ __forceinline__ void load(const char* const kb[4], const char* const vb[4], uint32_t koff,
                                          uint32_t voff, uint32_t voff1) {
@@ -100,7 +94,7 @@ struct Stage {
             }
         }
     }
-    // Zero V^T of tokens at or past valid[b] (the row's partial last block and
+    // Zero V of tokens at or past valid[b] (the row's partial last block and
     // blocks past its end, which hold whatever the clamped load read; 0 * NaN
     // is NaN).  Only the iteration that reaches the row's end calls this.
     __device__ __forceinline__ void mask_tail(const int valid[4], int t) {
@@ -118,19 +112,24 @@ struct Stage {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             st<u32x4_t>(ks + (b * kBS + (t >> 4)) * kKStride + (t & 15) * 8, k[b]);
-            uint16_t* vrow = vs + (b * kD + (t >> 1)) * kVStride + (t & 1) * 8;
-            st<u32x2_t>(vrow, u32x2_t{v[b][0], v[b][1]});
-            st<u32x2_t>(vrow + 4, u32x2_t{v[b][2], v[b][3]});
+            st<u32x4_t>(vs + b * kTile + (t >> 1) * kBS + (t & 1) * 8, v[b]);
         }
     }
 };
 
-// bf16 1.0 in both halves: the A operand of the "ones" tile whose product
-// with P^T is the row sum of P.
-constexpr uint32_t kOnes2 = 0x3F803F80u;
+// Score product operand row for lane row m (0..31) of a 32-key tile: bits 2
+// and 3 of the key index swapped.  Result register i of lane group g (lanes
+// 32 g .. 32 g + 31) then holds key 16 (i / 8) + 8 g + i % 8 of the tile.
+__device__ __forceinline__ int key_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int KV, int NT>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
+// Two probabilities as a bf16 pair, rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int KV>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
     constexpr int kElt = (KV == PKV_BF16) ? 2 : 1;
@@ -138,8 +137,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const int t = threadIdx.x;
     const int wave = t >> 6;
     const int lane = t & 63;
-    const int r = lane & 15;
-    const int g = lane >> 4;
+    const int c32 = lane & 31;  // score column = query row within the wave
+    const int g = lane >> 5;    // lane group
     // blockIdx -> (row, q tile, kv head), kv head fastest (one kv head per XCD).
     const int per_row = p.q_tiles * p.hkv;
     const int row = p.row0 + blockIdx.x / per_row;
@@ -149,20 +148,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 
     const int qbeg = p.cu_q[row];
     const int C = p.cu_q[row + 1] - qbeg;
-    const int j0 = qt * kQTile;
+    const int j0 = qt * p.tile_tokens;
     if (j0 >= C || qbeg < 0 || qbeg + C > p.total_q) return;  // (a malformed cu_q writes nothing)
     const int L = p.kv_lens[row];
     const bool row_ok = C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS;
     const int P = L - C;
-    const int jmax = min(j0 + kQTile, C);         // exclusive
+    const int jmax = min(j0 + p.tile_tokens, C);  // exclusive
     const int kend = row_ok ? P + jmax : 0;       // keys this tile needs
     const int n_iter = (kend + kKeys - 1) / kKeys;
     const int nblk_seq = (L + kBS - 1) / kBS;
     const int64_t blk_bytes = static_cast<int64_t>(p.hkv) * kTile * kElt;
     const int32_t* trow = p.table + static_cast<int64_t>(row) * p.max_blocks;
 
-    // this lane's query token (clamped for tile rows past the chunk's end)
-    const int j = min(j0 + r, C - 1);
+    // this lane's query row: token j0 + n / G, head n % G (tokens past the
+    // chunk's end are clamped and not stored)
+    const int n = 32 * wave + c32;
+    const int tok = n / p.group;
+    const int hh = n - tok * p.group;
+    const bool qrow_ok = tok < p.tile_tokens && j0 + tok < C;
+    const int j = min(j0 + tok, C - 1);
     const int qpos = P + j;  // keys 0..qpos are visible
 
     float scale = p.scale_log2;
@@ -172,32 +176,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
         vscale = p.v_scale[kvh];
     }
 
-    // Q^T operands of this wave's heads: Q[token j][head][32 ks + 8 g .. +7]
-    bf16x8_t qop[NT][4];
-    bool head_ok[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int hh = wave * NT + nt;
-        head_ok[nt] = hh < p.group;
+    // Q^T operand: Q[row][16 s + 8 g .. +7] for the 8 steps over d
+    bf16x8_t qop[8];
+    {
         const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                             (static_cast<int64_t>(qbeg + j) * p.hq + kvh * p.group + (head_ok[nt] ? hh : 0)) * kD;
+                             (static_cast<int64_t>(qbeg + j) * p.hq + kvh * p.group + hh) * kD;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            const u32x4_t x = head_ok[nt] ? ld<u32x4_t>(qp + 32 * k4 + 8 * g) : u32x4_t{0, 0, 0, 0};
-            qop[nt][k4] = __builtin_bit_cast(bf16x8_t, x);
+        for (int sd = 0; sd < 8; ++sd) {
+            const u32x4_t x = qrow_ok ? ld<u32x4_t>(qp + 16 * sd + 8 * g) : u32x4_t{0, 0, 0, 0};
+            qop[sd] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
 
-    // acc[nt][0..7]: O^T d-tiles; acc[nt][8]: the row sum of P (ones tile)
-    float m[NT];
-    f32x4_t acc[NT][9];
+    float m = -INFINITY;  // reference max (log2 units), same in both lane groups
+    float l = 0.f;        // this lane's part of the normaliser
+    f32x16_t acc[4];      // O^T d tiles: d = 32 dt + 8 (i / 4) + 4 g + i % 4
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        m[nt] = -INFINITY;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 9; ++i) acc[nt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{kOnes2, kOnes2, kOnes2, kOnes2});
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
     const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
@@ -205,6 +203,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const uint32_t voff = static_cast<uint32_t>(
         KV == PKV_BF16 ? ((t >> 1) * kBS + (t & 1) * 8) * kElt : fp8_v_offset(t >> 1, (t & 1) * 8));
     const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : fp8_v_offset(t >> 1, (t & 1) * 8 + 4));
+    // LDS element offsets of this lane's operands
+    const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
+    const int vrow0 = c32 * kBS + 8 * g;                // + b * kTile + (32 dt) * kBS
 
     // Tile addresses of iteration it's 4 blocks (uniform).  Blocks past the
     // row's end read its last block (their V is zeroed by mask_tail, their
@@ -239,89 +240,82 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
 
     // one iteration over the 64 keys staged in LDS buffer buf
     auto compute = [&](int it, int buf) {
-        const uint16_t* kc = ks[buf];
-        const uint16_t* vc = vs[buf];
+        const uint16_t* kc = ks[buf] + krow0;
+        const uint16_t* vc = vs[buf] + vrow0;
         const int kbase = it * kKeys;
-        // S^T tiles: s[nt][b] holds keys kbase + 16 b + 4 g + i for token row r
-        f32x4_t s[NT][4];
+        f32x16_t s[2];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) s[nt][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int sd = 0; sd < 8; ++sd) {
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ld<u32x4_t>(kc + (b * kBS + r) * kKStride + 32 * k4 + 8 * g));
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    s[nt][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[nt][k4], s[nt][b], 0, 0, 0);
+            for (int kt = 0; kt < 2; ++kt) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ld<u32x4_t>(kc + 32 * kt * kKStride + 16 * sd));
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[sd], s[kt], 0, 0, 0);
             }
         }
-        // online softmax per head tile.  Scores stay unscaled until the
-        // exponent (scale > 0, so the maximum commutes with it); keys can pass
-        // a query's position only in the iterations that reach the diagonal,
-        // so only those take the masked path (a uniform branch).
-        const bool need_mask = kbase + kKeys - 1 > P + j0;
-        bf16x8_t pb[NT][2];
+        // online softmax.  Scores stay unscaled until the exponent (scale >
+        // 0, so the maximum commutes with it); keys can pass a query's
+        // position only in the iterations that reach the diagonal, so only
+        // those take the masked path (a uniform branch).
+        float x[32];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float x[16];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int i = 0; i < 16; ++i) x[16 * kt + i] = s[kt][i];
+        if (kbase + kKeys - 1 > P + j0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[4 * b + i] = s[nt][b][i];
-            if (need_mask) {
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (kbase + 16 * b + 4 * g + i > qpos) x[4 * b + i] = -INFINITY;
-            }
-            float mb = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-            for (int i = 3; i < 16; i += 2) mb = fmaxf(fmaxf(mb, x[i]), x[i + 1 < 16 ? i + 1 : i]);
-            mb *= scale;
-            // lazy rescale (as in the decode kernel): only when some score
-            // passes the reference max by more than kLazy
-            if (__any(mb > m[nt] + kLazy)) {
-                mb = fmaxf(mb, __shfl_xor(mb, 16));
-                mb = fmaxf(mb, __shfl_xor(mb, 32));
-                const float mn = fmaxf(m[nt], mb);
-                const float alpha = __builtin_amdgcn_exp2f(m[nt] - mn);
-#pragma unroll
-                for (int i = 0; i < 9; ++i) acc[nt][i] *= alpha;
-                m[nt] = mn;
-            }
-            const float neg_m = -m[nt];
-            float pr[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale, neg_m));
-            // k-step h covers blocks 2h, 2h+1: this lane's 8 keys are
-            // (block 2h: 4g..4g+3, block 2h+1: 4g..4g+3)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) pb[nt][h] = to_bf16x8(pr + 8 * h);
+                for (int i = 0; i < 16; ++i)
+                    if (kbase + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7) > qpos) x[16 * kt + i] = -INFINITY;
         }
-        // O^T += V^T . P^T, and the row sum of P through the ones tile
+        float mb = x[0];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int i = 1; i < 31; i += 2) mb = fmaxf(fmaxf(mb, x[i]), x[i + 1]);
+        mb = fmaxf(mb, x[31]) * scale;
+        if (__any(mb > m + kLazy)) {  // rare: a new maximum for some row
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = fmaxf(m, mb);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+            m = mn;
+        }
+        const float neg_m = -m;
+        // P^T operand of step (kt, h): keys 32 kt + 16 h + 8 g .. +7
+        u32x4_t pk[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint16_t* v0 = vc + ((2 * h) * kD + 16 * mt + r) * kVStride + 4 * g;
-                const uint16_t* v1 = vc + ((2 * h + 1) * kD + 16 * mt + r) * kVStride + 4 * g;
-                const u32x2_t a0 = ld<u32x2_t>(v0);
-                const u32x2_t a1 = ld<u32x2_t>(v1);
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+                float pr[8];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nt][h], acc[nt][mt], 0, 0, 0);
+                for (int e = 0; e < 8; ++e)
+                    pr[e] = __builtin_amdgcn_exp2f(fmaf(x[16 * kt + 8 * h + e], scale, neg_m));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = pack_bf16(pr[2 * e], pr[2 * e + 1]);
+                    pk[kt][h][e] = w;
+                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l, false);
+                }
             }
-        }
+        // O^T += V^T . P^T: step (kt, h) covers block 2 kt + h
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[nt][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nt][h], acc[nt][8], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, pk[kt][h]);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8_t a =
+                        __builtin_bit_cast(bf16x8_t, ld<u32x4_t>(vc + (2 * kt + h) * kTile + 32 * dt * kBS));
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+                }
+            }
     };
 
     // One register stage and two LDS buffers: the loads for iteration it + 1
@@ -342,32 +336,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     }
 
     bad = bad || !row_ok;
-    const bool tok_ok = j0 + r < C;
+    l += __shfl_xor(l, 32);
+    if (!qrow_ok) return;
+    const float inv = bad ? __builtin_nanf("") : vscale / l;
+    uint16_t* op = static_cast<uint16_t*>(p.out) +
+                   (static_cast<int64_t>(qbeg + j) * p.hq + kvh * p.group + hh) * kD;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        if (!head_ok[nt] || !tok_ok) continue;
-        const float inv = bad ? __builtin_nanf("") : vscale / acc[nt][8][0];
-        const int hh = wave * NT + nt;
-        uint16_t* op = static_cast<uint16_t*>(p.out) +
-                       (static_cast<int64_t>(qbeg + j0 + r) * p.hq + kvh * p.group + hh) * kD;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const f32x4_t v = acc[nt][mt] * inv;
-            const uint32_t a = bf16_bits_rne(v[0]) | (bf16_bits_rne(v[1]) << 16);
-            const uint32_t b2 = bf16_bits_rne(v[2]) | (bf16_bits_rne(v[3]) << 16);
-            st<u32x2_t>(op + 16 * mt + 4 * g, u32x2_t{a, b2});
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const uint32_t a = bf16_bits_rne(acc[dt][4 * q4] * inv) | (bf16_bits_rne(acc[dt][4 * q4 + 1] * inv) << 16);
+            const uint32_t b2 =
+                bf16_bits_rne(acc[dt][4 * q4 + 2] * inv) | (bf16_bits_rne(acc[dt][4 * q4 + 3] * inv) << 16);
+            st<u32x2_t>(op + 32 * dt + 8 * q4 + 4 * g, u32x2_t{a, b2});
         }
-    }
-}
-
-template <int KV>
-void launch_prefill_kv(int nt, dim3 grid, hipStream_t s, const PrefillParams& p) {
-    switch (nt) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<KV, 1>), grid, dim3(256), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<KV, 2>), grid, dim3(256), 0, s, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<KV, 3>), grid, dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL((prefill_kernel<KV, 4>), grid, dim3(256), 0, s, p); break;
-    }
 }
 
 }  // namespace
@@ -399,8 +381,8 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     }
 
     const int32_t group = a->num_q_heads / c->num_kv_heads;
-    const int32_t nt = (group + 3) / 4;
-    const int32_t q_tiles = (a->max_q_len + pkv::kQTile - 1) / pkv::kQTile;
+    const int32_t tile_tokens = pkv::kRows / group;
+    const int32_t q_tiles = (a->max_q_len + tile_tokens - 1) / tile_tokens;
     const int64_t grid = static_cast<int64_t>(n_pre) * q_tiles * c->num_kv_heads;
     if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "prefill launch too large");
     const int64_t elt = c->kv_dtype == PKV_BF16 ? 2 : 1;
@@ -424,11 +406,12 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.max_kv_len = a->max_kv_len;
     p.q_tiles = q_tiles;
     p.total_q = a->total_q;
+    p.tile_tokens = tile_tokens;
     p.scale_log2 = pkv::kLog2e / sqrtf(static_cast<float>(pkv::kD));
     if (c->kv_dtype == PKV_BF16)
-        pkv::launch_prefill_kv<PKV_BF16>(nt, dim3(static_cast<unsigned>(grid)), s, p);
+        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     else
-        pkv::launch_prefill_kv<PKV_FP8_E4M3>(nt, dim3(static_cast<unsigned>(grid)), s, p);
+        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_FP8_E4M3>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
