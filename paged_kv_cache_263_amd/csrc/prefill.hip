@@ -15,8 +15,10 @@
 // all G heads each (128 rows), and wave w owns rows 32 w .. 32 w + 31 (row n
 // is token n / G, head n % G).  Per iteration the workgroup gathers 64 keys
 // (4 blocks, through the block table) into LDS - K as [key][d] with rows
-// padded to 136 elements (conflict-free operand reads), V as the cache's own
-// [d][16 tokens] tiles - double buffered, one barrier per iteration.  Each
+// padded to 136 elements, V as [d][16 tokens] tiles with the two 8-token
+// halves of a row swapped on alternate groups of 8 rows (both layouts keep the
+// operand reads free of bank conflicts) - double buffered, one barrier per
+// iteration.  Each
 // wave then computes, on the 32x32x16 bf16 matrix instruction:
 //   S^T[64 keys x 32 rows] = K . Q^T        (2 key tiles x 8 steps over d)
 //   O^T[128 x 32 rows]    += V^T . P^T      (4 d tiles x 4 steps of 16 keys)
@@ -26,7 +28,7 @@
 // key index swapped), so that the score registers come out holding, for each
 // 16-key step, exactly the 8 consecutive keys the P.V operand of that lane
 // needs: P goes from the score registers to the second product with no lane
-// exchange, and V is read in the cache's order.  P is rounded to bf16 once;
+// exchange, and V is read in the cache's token order.  P is rounded to bf16 once;
 // the normaliser sums the same rounded values (bf16 dot products with 1.0),
 // so the rounding largely cancels between numerator and denominator.
 // fp8 caches are converted to bf16 while staging (exact) with the per-head
@@ -66,6 +68,12 @@ struct PrefillParams {
     int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
 };
+
+// LDS element offset of tokens 8 h .. 8 h + 7 of d row d inside a staged V
+// tile: rows of 16 tokens, the two halves swapped in rows with bit 3 of d
+// set, so that the 16 lanes of one operand read (d rows r .. r + 15, same h)
+// cover all 64 banks.
+__device__ __forceinline__ int v_lds_offset(int d, int h) { return d * kBS + 8 * (h ^ ((d >> 3) & 1)); }
 
 // Staging registers for one iteration: thread t owns 16 bytes of each of the
 // iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V tiles
@@ -112,7 +120,7 @@ struct Stage {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             st<u32x4_t>(ks + (b * kBS + (t >> 4)) * kKStride + (t & 15) * 8, k[b]);
-            st<u32x4_t>(vs + b * kTile + (t >> 1) * kBS + (t & 1) * 8, v[b]);
+            st<u32x4_t>(vs + b * kTile + v_lds_offset(t >> 1, t & 1), v[b]);
         }
     }
 };
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : fp8_v_offset(t >> 1, (t & 1) * 8 + 4));
     // LDS element offsets of this lane's operands
     const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
-    const int vrow0 = c32 * kBS + 8 * g;                // + b * kTile + (32 dt) * kBS
+    const int vrow0 = v_lds_offset(c32, g);             // + b * kTile + (32 dt) * kBS
 
     // Tile addresses of iteration it's 4 blocks (uniform).  Blocks past the
     // row's end read its last block (their V is zeroed by mask_tail, their
