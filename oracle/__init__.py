@@ -14,6 +14,8 @@ Contents (each function cites the passage of the source pages it follows):
 * ``oracle.fp8``       - the OCP E4M3 (fp8) format written out from its
                          definition: decode of all 256 codes, round-to-nearest-
                          even quantisation with saturation.
+* ``oracle.int8``      - the symmetric INT8 storage (code * scale, round half to
+                         even, clamped to +-127) written out from its definition.
 * ``oracle.attention`` - softmax(q K^T / sqrt(d)) V in float64 for a decode
                          query and for a causal prefill chunk, with grouped-
                          query head sharing.
@@ -31,4 +33,4 @@ Every function in this package is pinned by tests under ``tests/`` marked
 for special cases, hand-worked fixtures under ``tests/golden/``).
 """
 
-from . import attention, fp8, pool  # noqa: F401
+from . import attention, fp8, int8, pool  # noqa: F401
