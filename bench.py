@@ -38,7 +38,8 @@ import torch
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "chunked")
+DTYPE_LABEL = {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "int8": "int8 kv / bf16 q"}
+WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "int8_long", "chunked")
 
 
 class TimingEvents:
@@ -99,7 +100,7 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
     ap.add_argument("--decode-parts", type=int, default=0, help="wavefronts per kv head (0 = auto)")
     ap.add_argument("--context", type=int, default=16384, help="chunked: cached context before the chunk")
-    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"), help="chunked: cache dtype")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8", "int8"), help="chunked: cache dtype")
     ap.add_argument("--fixed-len", type=int, default=0,
                     help="llama8b: every row this long instead of uniform 512..8192 (a balance control)")
     ap.add_argument("--placement", default="shuffled", choices=("shuffled", "identity"),
@@ -120,10 +121,11 @@ def build_workload(name: str, args=None):
 
     if name == "chunked":
         w = W.chunked(context=args.context)
-        return W.scaled_fp8(w) if args.kv == "fp8" else w
+        return {"fp8": W.scaled_fp8, "int8": W.scaled_int8}.get(args.kv, lambda x: x)(w)
     if name == "llama8b" and args is not None and args.fixed_len:
         return W.llama8b(min_len=args.fixed_len, max_len=args.fixed_len)
-    return {"llama8b": W.llama8b, "shared_prefix": W.shared_prefix, "fp8_long": W.fp8_long}[name]()
+    return {"llama8b": W.llama8b, "shared_prefix": W.shared_prefix, "fp8_long": W.fp8_long,
+            "int8_long": W.int8_long}[name]()
 
 
 def describe(w) -> str:
@@ -134,6 +136,8 @@ def describe(w) -> str:
                          "suffix 50-1000, 64 q / 8 kv heads, bf16, one copy-on-write",
         "fp8_long": "long-context fp8 paged decode: batch 16, KV length 131072, 64 q / 8 kv heads, fp8 E4M3 K/V "
                     "with per-head fp32 scales, bf16 Q",
+        "int8_long": "long-context int8 paged decode: batch 16, KV length 131072, 64 q / 8 kv heads, int8 K/V "
+                     "with per-head fp32 scales, bf16 Q",
         "chunked": "chunked prefill: one 1024-query causal chunk over cached context, batched with 32 decode "
                    "rows of 4096 tokens, 64 q / 8 kv heads, d 128",
     }[w.name]
@@ -189,7 +193,7 @@ def run_chunked(args, w, device):
         "metric": "chunked prefill + decode rows: prefill TFLOP/s (causal algorithmic flops)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(dt * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 kv / bf16 q",
+        "vs_baseline": None, "dtype": DTYPE_LABEL[w.kv_dtype],
         "data": "synthetic",
         "config": {"workload": describe(w), "context": P, "chunk": C, "decode_rows": nd},
         "kernels_us": {"decode_part": round(dec_ms * 1e3, 2), "prefill": round(pre_ms * 1e3, 2)},
@@ -209,7 +213,7 @@ def setup(w, device):
 
     pool = pk.kv_pool_create(w.num_blocks, w.placement)
     ks = vs = None
-    if w.kv_dtype == "fp8":
+    if w.kv_dtype in ("fp8", "int8"):
         ks, vs = w.k_scale.reshape(1, -1), w.v_scale.reshape(1, -1)
     cache = pk.KVCache(w.kv_dtype, 1, w.num_blocks, w.hkv, device, k_scale=ks, v_scale=vs, zero=False)
     lens, starts = W.replay_lengths(w)
@@ -235,7 +239,7 @@ def cpu_baseline(w, device, rows: int, budget_s: float = 10.0):
     """The oracle as it stands, on a bounded sample of the same workload: the
     oracle's pool model replays the script; then, row after row (the first
     ``rows`` batch rows, in full passes, at most three), it reads each row's
-    K/V through its own table (fp8: through its own codec) and computes fp64
+    K/V through its own table (fp8, int8: through its own codecs) and computes fp64
     attention for all query heads, until ``budget_s`` seconds of oracle time
     have accumulated.  Reported in the metric's unit: KV bytes covered /
     oracle seconds.  Input generation and host transfer are not timed."""
@@ -244,6 +248,7 @@ def cpu_baseline(w, device, rows: int, budget_s: float = 10.0):
     import workloads as W
     from oracle import attention as OA
     from oracle import fp8 as OF
+    from oracle import int8 as OI
     from oracle import pool as OP
 
     model = OP.PoolModel(w.num_blocks, order=w.placement)
@@ -292,9 +297,11 @@ def cpu_baseline(w, device, rows: int, budget_s: float = 10.0):
             for oid, (k, v) in vals.items():
                 sel = np.nonzero(op_ids == oid)[0]
                 kk, vv = k[offs[sel]], v[offs[sel]]
-                if w.kv_dtype == "fp8":
-                    kk = OF.dequantise(OF.quantise_scaled(kk, w.k_scale[None, :, None]), w.k_scale[None, :, None])
-                    vv = OF.dequantise(OF.quantise_scaled(vv, w.v_scale[None, :, None]), w.v_scale[None, :, None])
+                codec = {"fp8": OF, "int8": OI}.get(w.kv_dtype)
+                if codec is not None:
+                    ks, vs = w.k_scale[None, :, None], w.v_scale[None, :, None]
+                    kk = codec.dequantise(codec.quantise_scaled(kk, ks), ks)
+                    vv = codec.dequantise(codec.quantise_scaled(vv, vs), vs)
                 K[sel], V[sel] = kk, vv
             OA.decode(q, K, V)
             spent += time.perf_counter() - t0
@@ -403,7 +410,7 @@ def recorded_traffic():
 
 
 def elt_bytes(w) -> int:
-    return {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
 
 
 def main():
@@ -523,7 +530,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "f32": "f32"}[w.kv_dtype],
+        "dtype": DTYPE_LABEL[w.kv_dtype],
         "data": "synthetic",
         "config": {"workload": describe(w), "batch": B, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "block_size": 16, "mean_kv_len": round(float(np.mean(lens)), 1),
@@ -542,7 +549,7 @@ def main():
         "host_us_per_step": round(host * 1e6 / args.steps, 1),
     }
     if not args.no_cpu_baseline:
-        rows = args.cpu_sample_rows or {"llama8b": 64, "shared_prefix": 256, "fp8_long": 2}[w.name]
+        rows = args.cpu_sample_rows or {"llama8b": 64, "shared_prefix": 256, "fp8_long": 2, "int8_long": 2}[w.name]
         result["cpu_baseline"] = cpu_baseline(w, device, rows)
     print(json.dumps(result), flush=True)
 

@@ -50,7 +50,7 @@ enum {
     PKV_ERR_WORKSPACE = -6    /* workspace missing or smaller than paged_attn_workspace_size() */
 };
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2, PKV_INT8 = 3 } pkv_dtype;
 
 /* ------------------------------------------------------------------------
  * Host block allocator, sequences and block tables
@@ -150,12 +150,14 @@ int block_table_build(const pkv_pool* pool, const int32_t* seqs, int32_t n, int3
  *   k_pool: [num_layers][num_blocks][num_kv_heads][16 tokens][head_dim]
  *   v_pool: [num_layers][num_blocks][num_kv_heads][head_dim][16 tokens]
  * (V is stored token-minor inside a block so that the P.V contraction over
- * tokens reads contiguous memory.)  fp8 V tiles (16 x 128 codes, 2 KiB) keep
- * (d, token) at byte (token / 4) * 512 + (d % 16) * 32 + (d / 16) * 4 +
- * token % 4, so the decode kernel reads them with 16-byte loads.
- * Elements are kv_dtype.  For fp8, stored value = e4m3(code) * scale with
- * one fp32 scale per (layer, kv head) for K (k_scale [num_layers]
- * [num_kv_heads]) and for V (v_scale); NULL otherwise. */
+ * tokens reads contiguous memory.)  One-byte V tiles (fp8 and int8: 16 x 128
+ * codes, 2 KiB) keep (d, token) at byte (token / 4) * 512 + (d % 16) * 32 +
+ * (d / 16) * 4 + token % 4, so the decode kernel reads them with 16-byte
+ * loads.  Elements are kv_dtype.  Stored value = e4m3(code) * scale for fp8
+ * ([P2] "Quantising the cache") and code * scale for int8 (a signed byte in
+ * -127..127; [P3] "M.65 Inference Serving", quantisation of the KV cache),
+ * with one fp32 scale per (layer, kv head) for K (k_scale [num_layers]
+ * [num_kv_heads]) and for V (v_scale); NULL for f32 and bf16. */
 typedef struct {
     int32_t kv_dtype;     /* pkv_dtype */
     int32_t num_layers;
@@ -170,7 +172,8 @@ typedef struct {
 } pkv_cache;
 
 /* Arguments of an attention call.  Supported (q_dtype, kv_dtype) pairs:
- * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).  out has q's dtype and shape.
+ * (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (BF16, INT8).  out has q's
+ * dtype and shape.
  * GQA: query head h reads kv head h / (num_q_heads / num_kv_heads). */
 typedef struct {
     int32_t layer;
@@ -192,8 +195,8 @@ typedef struct {
     /* tuning and scratch: */
     int32_t decode_parts;        /* decode: the blocks of each kv head are divided evenly among this
                                     many wavefronts (<= 4096, and at most one per 8 blocks of the
-                                    head's work); 0 = auto (8 per compute unit in all, 12 for an
-                                    fp8 cache) */
+                                    head's work); 0 = auto (8 per compute unit in all, 12 for a
+                                    one-byte cache) */
     void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
@@ -226,14 +229,15 @@ int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* s
  * C_i = cu_q[i+1]-cu_q[i] queries that are the last C_i of its kv_lens[i]
  * cached tokens (their K/V already written), and query j attends keys
  * 0..kv_lens[i]-C_i+j (causal, bottom-right aligned).  Chunk rows need a
- * bf16 or fp8 cache (PKV_ERR_UNSUPPORTED for fp32).  A chunk row with an
+ * bf16, fp8 or int8 cache (PKV_ERR_UNSUPPORTED for fp32).  A chunk row with an
  * invalid length or block id gets NaN output. */
 int paged_attn_prefill_chunk(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
 /* Write n_tokens new tokens' K and V into the cache at their slots (fp8:
- * code = e4m3 round-to-nearest-even of fp32(x / scale), saturating at +-448).
+ * code = e4m3 round-to-nearest-even of fp32(x / scale), saturating at +-448;
+ * int8: code = fp32(x / scale) rounded half to even, clamped to +-127).
  *   k_new, v_new: device [n_tokens][num_kv_heads][head_dim] of val_dtype
- *                 (F32 for an F32 cache, BF16 for BF16 and FP8 caches)
+ *                 (F32 for an F32 cache, BF16 for BF16, FP8 and INT8 caches)
  *   slots:        [n_tokens], slot = block*16 + offset (from seq_append)
  * slots, rows and positions may be device memory or pinned host memory mapped
  * for the device (hipHostMalloc); the kernel then reads them over the host

@@ -28,7 +28,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
-PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 HEAD_DIM = 128
 _STATUS = {0: "OK", -1: "INVALID", -2: "OOM", -3: "STATE", -4: "UNSUPPORTED", -5: "HIP", -6: "WORKSPACE"}
@@ -302,9 +302,9 @@ def block_table_build(pool: Pool, seqs, max_blocks: int):
 # ---------------------------------------------------------------------------
 # device cache and kernels
 
-_DT = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}
+_DT = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8, PKV_INT8: torch.int8}
 _QDT = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
-_NAMES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}
+_NAMES = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3, "int8": PKV_INT8}
 
 
 class KVCache:
@@ -312,7 +312,8 @@ class KVCache:
 
     k_pool: [layers, num_blocks, kv_heads, 16, 128]; v_pool: [layers, num_blocks,
     kv_heads, 128, 16] (token-minor inside a block); fp8 pools hold E4M3 codes
-    as uint8 with fp32 scales [layers, kv_heads] for K and V."""
+    as uint8 and int8 pools signed codes as int8, each with fp32 scales
+    [layers, kv_heads] for K and V."""
 
     def __init__(self, kv_dtype, num_layers: int, num_blocks: int, num_kv_heads: int, device="cuda",
                  k_scale=None, v_scale=None, zero: bool = True):
@@ -323,9 +324,9 @@ class KVCache:
         self.k_pool = alloc((num_layers, num_blocks, num_kv_heads, BLOCK_SIZE, HEAD_DIM), dtype=dt, device=device)
         self.v_pool = alloc((num_layers, num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE), dtype=dt, device=device)
         self.k_scale = self.v_scale = None
-        if self.kv_dtype == PKV_FP8_E4M3:
+        if self.kv_dtype in (PKV_FP8_E4M3, PKV_INT8):
             if k_scale is None or v_scale is None:
-                raise PagedKVError(-1, "fp8 cache needs k_scale and v_scale")
+                raise PagedKVError(-1, "fp8 and int8 caches need k_scale and v_scale")
             self.k_scale = torch.as_tensor(k_scale, dtype=torch.float32).reshape(num_layers, num_kv_heads).to(device)
             self.v_scale = torch.as_tensor(v_scale, dtype=torch.float32).reshape(num_layers, num_kv_heads).to(device)
         self._desc = pkv_cache(self.kv_dtype, num_layers, num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE,

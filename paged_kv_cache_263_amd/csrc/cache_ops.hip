@@ -1,12 +1,14 @@
-// Writes into the paged cache: new tokens' K/V to their slots (with fp8
-// quantisation on write), and whole-block copies for copy-on-write.
+// Writes into the paged cache: new tokens' K/V to their slots (with fp8 or
+// int8 quantisation on write), and whole-block copies for copy-on-write.
 //
 // A new block is needed every 16 tokens and a token's slot comes from the
 // host allocator ([P3] "PagedAttention block management", item (c)); a
 // sequence that must write into a shared block first gets its own copy ([P2]
 // "Sharing, and what makes a prefix reusable"; [P3] item (g)).  The fp8 cache
 // stores one byte per element ([P2] "Quantising the cache"): code = E4M3
-// round-to-nearest-even of fp32(x / scale), saturating at +-448.
+// round-to-nearest-even of fp32(x / scale), saturating at +-448.  The int8
+// cache ([P3] "M.65 Inference Serving", quantising the KV cache) stores
+// code = fp32(x / scale) rounded half to even, clamped to +-127.
 #include <type_traits>
 
 #include "device.h"
@@ -32,9 +34,14 @@ struct WriteParams {
 
 // Four consecutive d of one head of one token: the values as read, and
 // their stores into the K tile ([16][128]) and the V tile ([128][16]; fp8:
-// fp8_v_offset).
+// byte_v_offset).
 template <int KV>
 struct Quad {
+    // one-byte code of a value already divided by its scale
+    static __device__ __forceinline__ uint32_t code(float x) {
+        if constexpr (KV == PKV_INT8) return int8_code_rne(x);
+        else return e4m3_code_rne(x);
+    }
     using T = typename std::conditional<KV == PKV_F32, f32x4_t, u32x2_t>::type;  // 4 f32 or 4 bf16
     T k, v;
     __device__ __forceinline__ void load(const WriteParams& p, int64_t e) {  // e: element index, multiple of 4
@@ -69,8 +76,8 @@ struct Quad {
             for (int j = 0; j < 4; ++j) {
                 const float xk = __uint_as_float((k[j >> 1] >> (16 * (j & 1))) << 16);
                 const float xv = __uint_as_float((v[j >> 1] >> (16 * (j & 1))) << 16);
-                kc |= e4m3_code_rne(xk / ks) << (8 * j);
-                vp[fp8_v_offset(d + j, o)] = static_cast<uint8_t>(e4m3_code_rne(xv / vs));
+                kc |= code(xk / ks) << (8 * j);
+                vp[byte_v_offset(d + j, o)] = static_cast<uint8_t>(code(xv / vs));
             }
             st<uint32_t>(kp + o * kD + d, kc);
         }
@@ -174,7 +181,10 @@ int kv_cache_write(const pkv_cache* c, int32_t layer, int32_t n_tokens, int32_t 
     switch (c->kv_dtype) {
         case PKV_F32: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_F32>, dim3(n_tokens), dim3(256), 0, s, p); break;
         case PKV_BF16: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_BF16>, dim3(n_tokens), dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_FP8_E4M3>, dim3(n_tokens), dim3(256), 0, s, p); break;
+        case PKV_FP8_E4M3:
+            hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_FP8_E4M3>, dim3(n_tokens), dim3(256), 0, s, p);
+            break;
+        default: hipLaunchKernelGGL(pkv::kv_write_kernel<PKV_INT8>, dim3(n_tokens), dim3(256), 0, s, p); break;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));

@@ -7,7 +7,7 @@ int check_cache(const pkv_cache* c) {
     if (!c) return fail(PKV_ERR_INVALID, "null cache descriptor");
     if (c->block_size != PKV_BLOCK_SIZE) return fail(PKV_ERR_UNSUPPORTED, "block size %d (only 16)", c->block_size);
     if (c->head_dim != PKV_HEAD_DIM) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (only 128)", c->head_dim);
-    if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_FP8_E4M3)
+    if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_FP8_E4M3 && c->kv_dtype != PKV_INT8)
         return fail(PKV_ERR_INVALID, "unknown kv dtype %d", c->kv_dtype);
     if (c->num_layers <= 0 || c->num_blocks <= 0 || c->num_kv_heads <= 0)
         return fail(PKV_ERR_INVALID, "bad cache shape (layers %d, blocks %d, kv heads %d)", c->num_layers,
@@ -15,8 +15,8 @@ int check_cache(const pkv_cache* c) {
     if (static_cast<int64_t>(c->num_blocks) * PKV_BLOCK_SIZE > INT32_MAX)
         return fail(PKV_ERR_INVALID, "too many blocks for int32 slots");
     if (!c->k_pool || !c->v_pool) return fail(PKV_ERR_INVALID, "null K or V pool");
-    if (c->kv_dtype == PKV_FP8_E4M3 && (!c->k_scale || !c->v_scale))
-        return fail(PKV_ERR_INVALID, "fp8 cache needs k_scale and v_scale");
+    if ((c->kv_dtype == PKV_FP8_E4M3 || c->kv_dtype == PKV_INT8) && (!c->k_scale || !c->v_scale))
+        return fail(PKV_ERR_INVALID, "fp8 and int8 caches need k_scale and v_scale");
     return PKV_OK;
 }
 
@@ -26,7 +26,8 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
     if (!a) return fail(PKV_ERR_INVALID, "null attention arguments");
     if (a->layer < 0 || a->layer >= c->num_layers) return fail(PKV_ERR_INVALID, "layer %d out of range", a->layer);
     const bool ok = (a->q_dtype == PKV_F32 && c->kv_dtype == PKV_F32) ||
-                    (a->q_dtype == PKV_BF16 && (c->kv_dtype == PKV_BF16 || c->kv_dtype == PKV_FP8_E4M3));
+                    (a->q_dtype == PKV_BF16 && (c->kv_dtype == PKV_BF16 || c->kv_dtype == PKV_FP8_E4M3 ||
+                                                c->kv_dtype == PKV_INT8));
     if (!ok) return fail(PKV_ERR_UNSUPPORTED, "q dtype %d with kv dtype %d", a->q_dtype, c->kv_dtype);
     if (a->num_q_heads <= 0 || a->num_q_heads % c->num_kv_heads != 0)
         return fail(PKV_ERR_INVALID, "%d query heads is not a multiple of %d kv heads", a->num_q_heads, c->num_kv_heads);

@@ -25,9 +25,9 @@
 // contiguous 16 / 8 / 4-byte load and a wave reads each 4 KiB (bf16) tile in
 // whole cache lines.  P is split into a bf16 high part and a bf16 remainder,
 // so P.V keeps ~16 mantissa bits.  fp32 caches use the fp32 matrix
-// instruction (16x16x4) with the same lanes; fp8 caches convert E4M3 bytes
-// to bf16 in registers (exact) and fold the per-head scales into the score
-// scale (K) and the final normalisation (V).
+// instruction (16x16x4) with the same lanes; one-byte caches (fp8 E4M3 and
+// int8) convert their codes to bf16 in registers (exact) and fold the
+// per-head scales into the score scale (K) and the final normalisation (V).
 //
 // Work division.  Rows have very different lengths, so fixed-size chunks per
 // row leave some wavefronts long tails of work while others sit idle.  Here
@@ -57,7 +57,7 @@ struct DecodeParams {
     void* out;                      // [rows][hq][128]
     const void* k_pool;             // this layer: [num_blocks][hkv][16][128]
     const void* v_pool;             // this layer: [num_blocks][hkv][128][16]
-    const float* k_scale;           // this layer: [hkv] (fp8 only)
+    const float* k_scale;           // this layer: [hkv] (one-byte caches only)
     const float* v_scale;
     const int32_t* __restrict__ table;    // [rows][max_blocks]
     const int32_t* __restrict__ kv_lens;  // [rows]
@@ -159,14 +159,15 @@ struct Tile<PKV_BF16> {
     }
 };
 
-// fp8 tiles are read with 16-byte loads (narrower loads cap the read rate
-// well below the HBM rate).  K: lane (r, g) reads codes 32 g .. 32 g + 31 of
-// token row r, and matrix step ks takes codes 32 g + 8 ks .. +7; the query
+// One-byte (fp8, int8) tiles are read with 16-byte loads (narrower loads cap
+// the read rate well below the HBM rate).  K: lane (r, g) reads codes 32 g ..
+// 32 g + 31 of token row r, and matrix step ks takes codes 32 g + 8 ks .. +7;
+// the query
 // operand uses the same order of d (a permutation of the contraction index,
-// so the scores are unchanged).  V: the tile layout of fp8_v_offset puts the
+// so the scores are unchanged).  V: the tile layout of byte_v_offset puts the
 // lane's 8 words (tokens 4g..4g+3 of d rows 16 n + r) in 32 contiguous bytes.
-template <>
-struct Tile<PKV_FP8_E4M3> {
+template <int KV>
+struct ByteTile {
     using Elt = uint8_t;
     using Q = bf16x8_t[4];
     u32x4_t k[2];  // codes 32 g .. 32 g + 31 of token row r
@@ -194,8 +195,8 @@ struct Tile<PKV_FP8_E4M3> {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const u32x2_t a = fp8x4_to_bf16x4(k[ks >> 1][2 * (ks & 1)]);
-            const u32x2_t b = fp8x4_to_bf16x4(k[ks >> 1][2 * (ks & 1) + 1]);
+            const u32x2_t a = byte4_to_bf16x4<KV>(k[ks >> 1][2 * (ks & 1)]);
+            const u32x2_t b = byte4_to_bf16x4<KV>(k[ks >> 1][2 * (ks & 1) + 1]);
             const u32x4_t kb = {a[0], a[1], b[0], b[1]};
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), q[ks], s, 0, 0, 0);
         }
@@ -206,12 +207,17 @@ struct Tile<PKV_FP8_E4M3> {
         split_p(p, hi, lo);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-            const i16x4_t a = __builtin_bit_cast(i16x4_t, fp8x4_to_bf16x4(v[n >> 2][n & 3]));
+            const i16x4_t a = __builtin_bit_cast(i16x4_t, byte4_to_bf16x4<KV>(v[n >> 2][n & 3]));
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[n], 0, 0, 0);
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[n], 0, 0, 0);
         }
     }
 };
+
+template <>
+struct Tile<PKV_FP8_E4M3> : ByteTile<PKV_FP8_E4M3> {};
+template <>
+struct Tile<PKV_INT8> : ByteTile<PKV_INT8> {};
 
 template <>
 struct Tile<PKV_F32> {
@@ -446,7 +452,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
     float scale = p.scale_log2;
     float vs = 1.f;
-    if constexpr (KV == PKV_FP8_E4M3) {
+    if constexpr (is_byte_dtype(KV)) {
         scale *= p.k_scale[kvh];
         vs = p.v_scale[kvh];
     }
@@ -626,15 +632,15 @@ int decode_pipeline_depth() {
 }
 
 // Wavefronts per kv head: PKV_DECODE_WAVES_PER_CU wavefronts per compute
-// unit in total (default 8; 12 for an fp8 cache, whose blocks carry half the
-// bytes for the same instruction count), shared among the kv heads.
+// unit in total (default 8; 12 for a one-byte cache, whose blocks carry half
+// the bytes for the same instruction count), shared among the kv heads.
 int decode_parts_auto(int hkv, int kv_dtype) {
     static const int env = [] {
         const char* e = std::getenv("PKV_DECODE_WAVES_PER_CU");
         const int v = e ? std::atoi(e) : 0;
         return v < 0 ? 0 : (v > 32 ? 32 : v);
     }();
-    const int per_cu = env > 0 ? env : (kv_dtype == PKV_FP8_E4M3 ? 12 : 8);
+    const int per_cu = env > 0 ? env : (is_byte_dtype(kv_dtype) ? 12 : 8);
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -656,10 +662,13 @@ void launch_decode_kernel(int kv_dtype, int depth, dim3 grid, hipStream_t stream
             else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 3, LOCAL>), grid, dim3(64), 0, stream, p);
             else hipLaunchKernelGGL((decode_kernel<PKV_BF16, 4, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
-        default:
+        case PKV_FP8_E4M3:
             if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 2, LOCAL>), grid, dim3(64), 0, stream, p);
             else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 3, LOCAL>), grid, dim3(64), 0, stream, p);
             else hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 4, LOCAL>), grid, dim3(64), 0, stream, p);
+            break;
+        default:
+            hipLaunchKernelGGL((decode_kernel<PKV_INT8, 2, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
     }
 }

@@ -50,12 +50,42 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
                    __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u)};
 }
 
-// Byte offset of (d row, token) inside one fp8 V tile (2 KiB): tokens in
+// Four int8 codes -> four bf16 (exact: every integer in -127..127 has at
+// most 7 significant bits).  Each byte converts sign-extended to fp32 and the
+// high halves are packed as in fp8x4_to_bf16x4.
+__device__ __forceinline__ u32x2_t int8x4_to_bf16x4(uint32_t w) {
+    const float f0 = static_cast<float>(static_cast<int8_t>(w & 0xFFu));
+    const float f1 = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xFFu));
+    const float f2 = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xFFu));
+    const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
+    return u32x2_t{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+                   __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u)};
+}
+
+// fp32 -> int8 code (as the low byte): nearest integer, ties to even,
+// clamped to -127..127.
+__device__ __forceinline__ uint32_t int8_code_rne(float x) {
+    const float r = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+    return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+}
+
+// One-byte cache dtypes (codes times a per-(layer, kv head) fp32 scale).
+constexpr bool is_byte_dtype(int kv) { return kv == PKV_FP8_E4M3 || kv == PKV_INT8; }
+
+// Four one-byte codes of the cache's dtype -> four bf16.
+template <int KV>
+__device__ __forceinline__ u32x2_t byte4_to_bf16x4(uint32_t w) {
+    if constexpr (KV == PKV_INT8) return int8x4_to_bf16x4(w);
+    else return fp8x4_to_bf16x4(w);
+}
+
+// Byte offset of (d row, token) inside a one-byte (fp8 or int8) V tile
+// (2 KiB): tokens in
 // groups of 4, then d % 16, then d / 16, then the token within its group.
 // Lane (r, g) of the decode kernel then finds the 8 words it feeds to the
 // matrix cores - tokens 4g..4g+3 of d rows 16 n + r, n = 0..7 - in 32
 // contiguous bytes at g * 512 + r * 32, read as two 16-byte loads.
-__device__ __forceinline__ int fp8_v_offset(int d, int tok) {
+__device__ __forceinline__ int byte_v_offset(int d, int tok) {
     return (tok >> 2) * 512 + (d & 15) * 32 + (d >> 4) * 4 + (tok & 3);
 }
 

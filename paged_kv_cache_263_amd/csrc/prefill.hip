@@ -31,8 +31,8 @@
 // exchange, and V is read in the cache's token order.  P is rounded to bf16 once;
 // the normaliser sums the same rounded values (bf16 dot products with 1.0),
 // so the rounding largely cancels between numerator and denominator.
-// fp8 caches are converted to bf16 while staging (exact) with the per-head
-// scales folded into the score scale and the output.
+// fp8 and int8 caches are converted to bf16 while staging (exact) with the
+// per-head scales folded into the score scale and the output.
 #include <cmath>
 
 #include "device.h"
@@ -77,14 +77,15 @@ __device__ __forceinline__ int v_lds_offset(int d, int h) { return d * kBS + 8 *
 
 // Staging registers for one iteration: thread t owns 16 bytes of each of the
 // iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V tiles
-// (d row t/2, tokens (t%2)*8..+7); fp8 codes are converted to bf16 on load.
+// (d row t/2, tokens (t%2)*8..+7); one-byte codes are converted to bf16 on
+// load.
 // The tile addresses are uniform (one per block) and the thread's offset
 // inside a tile is fixed, so a load costs no vector arithmetic.
 template <int KV>
 struct Stage {
     u32x4_t k[4], v[4];
-    // voff: this thread's V piece (bf16); fp8 tiles keep it as two 4-byte
-    // words at voff and voff1 (fp8_v_offset)
+    // voff: this thread's V piece (bf16); one-byte tiles keep it as two 4-byte
+    // words at voff and voff1 (byte_v_offset)
     __device__ __forceinline__ void load(const char* const kb[4], const char* const vb[4], uint32_t koff,
                                          uint32_t voff, uint32_t voff1) {
 #pragma unroll
@@ -95,8 +96,8 @@ struct Stage {
             } else {
                 const u32x2_t kk = ld<u32x2_t>(kb[b] + koff);
                 const u32x2_t vv = {ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1)};
-                const u32x2_t k0 = fp8x4_to_bf16x4(kk[0]), k1 = fp8x4_to_bf16x4(kk[1]);
-                const u32x2_t v0 = fp8x4_to_bf16x4(vv[0]), v1 = fp8x4_to_bf16x4(vv[1]);
+                const u32x2_t k0 = byte4_to_bf16x4<KV>(kk[0]), k1 = byte4_to_bf16x4<KV>(kk[1]);
+                const u32x2_t v0 = byte4_to_bf16x4<KV>(vv[0]), v1 = byte4_to_bf16x4<KV>(vv[1]);
                 k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
                 v[b] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
             }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
     float scale = p.scale_log2;
     float vscale = 1.f;
-    if constexpr (KV == PKV_FP8_E4M3) {
+    if constexpr (is_byte_dtype(KV)) {
         scale *= p.k_scale[kvh];
         vscale = p.v_scale[kvh];
     }
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const uint32_t koff = static_cast<uint32_t>(((t >> 4) * kD + (t & 15) * 8) * kElt);
     const uint32_t voff = static_cast<uint32_t>(
-        KV == PKV_BF16 ? ((t >> 1) * kBS + (t & 1) * 8) * kElt : fp8_v_offset(t >> 1, (t & 1) * 8));
-    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : fp8_v_offset(t >> 1, (t & 1) * 8 + 4));
+        KV == PKV_BF16 ? ((t >> 1) * kBS + (t & 1) * 8) * kElt : byte_v_offset(t >> 1, (t & 1) * 8));
+    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(t >> 1, (t & 1) * 8 + 4));
     // LDS element offsets of this lane's operands
     const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
     const int vrow0 = v_lds_offset(c32, g);             // + b * kTile + (32 dt) * kBS
@@ -369,7 +370,7 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     int st = pkv::check_attn(c, a);
     if (st) return st;
     if (a->num_seqs == 0) return PKV_OK;
-    if (c->kv_dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "chunked prefill supports bf16 and fp8 caches");
+    if (c->kv_dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "chunked prefill supports bf16, fp8 and int8 caches");
     if (!a->cu_q) return fail(PKV_ERR_INVALID, "prefill needs cu_q");
     if (a->num_decode < 0 || a->num_decode > a->num_seqs) return fail(PKV_ERR_INVALID, "bad num_decode %d", a->num_decode);
     const int32_t n_pre = a->num_seqs - a->num_decode;
@@ -418,8 +419,10 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.scale_log2 = pkv::kLog2e / sqrtf(static_cast<float>(pkv::kD));
     if (c->kv_dtype == PKV_BF16)
         hipLaunchKernelGGL(pkv::prefill_kernel<PKV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
-    else
+    else if (c->kv_dtype == PKV_FP8_E4M3)
         hipLaunchKernelGGL(pkv::prefill_kernel<PKV_FP8_E4M3>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_INT8>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -7,7 +7,7 @@ its attention kernels produce the outputs under test.
 Oracle side: the oracle's pool model replays the same script; a token store
 records, for every slot, which generated value was written there (op id and
 offset), so a row's K/V are read back through the oracle's own tables; fp8
-values are quantised by the oracle's codec.  Attention is the oracle's fp64
+and int8 values are quantised by the oracle's codecs.  Attention is the oracle's fp64
 definition.  Nothing on this side reads anything the HIP side produced.
 """
 
@@ -19,9 +19,12 @@ import torch
 import workloads as W
 from oracle import attention as OA
 from oracle import fp8 as OF
+from oracle import int8 as OI
 from oracle import pool as OP
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# int8 codes convert to bf16 exactly, so an int8 cache runs the bf16 path's
+# arithmetic on the same stored values: the bf16 bound applies.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 2e-2}
 
 
 def blocks(n: int) -> int:
@@ -39,7 +42,7 @@ class HipSide:
         order = w.placement if placement is None else placement
         self.pool = pk.kv_pool_create(w.num_blocks, order)
         ks = vs = None
-        if w.kv_dtype == "fp8":
+        if w.kv_dtype in ("fp8", "int8"):
             ks = np.tile(w.k_scale, (num_layers, 1))
             vs = np.tile(w.v_scale, (num_layers, 1))
         self.cache = pk.KVCache(w.kv_dtype, num_layers, w.num_blocks, w.hkv, device, k_scale=ks, v_scale=vs)
@@ -147,9 +150,10 @@ class OracleSide:
             idx = torch.as_tensor(offs[sel], device=k.device)
             kk = k[idx, kvh].float().cpu().numpy()
             vv = v[idx, kvh].float().cpu().numpy()
-            if self.w.kv_dtype == "fp8":
-                kk = OF.dequantise(OF.quantise_scaled(kk, self.w.k_scale[kvh]), self.w.k_scale[kvh])
-                vv = OF.dequantise(OF.quantise_scaled(vv, self.w.v_scale[kvh]), self.w.v_scale[kvh])
+            codec = {"fp8": OF, "int8": OI}.get(self.w.kv_dtype)
+            if codec is not None:
+                kk = codec.dequantise(codec.quantise_scaled(kk, self.w.k_scale[kvh]), self.w.k_scale[kvh])
+                vv = codec.dequantise(codec.quantise_scaled(vv, self.w.v_scale[kvh]), self.w.v_scale[kvh])
             K[sel] = kk
             V[sel] = vv
         return K, V

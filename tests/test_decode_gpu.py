@@ -1,11 +1,11 @@
 """GPU parity of paged decode (through the C ABI) against the fp64 oracle.
 
-Tolerances (max abs error): 1e-5 for fp32, 2e-2 for bf16, 6e-2 for an fp8
-cache.  Every workload also runs "peaked" (queries x4, outputs O(1)) and
+Tolerances (max abs error): 1e-5 for fp32, 2e-2 for bf16 and for an int8
+cache (its codes convert to bf16 exactly), 6e-2 for an fp8 cache.  Every workload also runs "peaked" (queries x4, outputs O(1)) and
 "needle" (planted keys at block, chunk and sequence edges) forms, because
 under N(0, 1) inputs the outputs are small enough that a tolerance alone
-would not catch a wrong block or head mapping.  Block tables and fp8 codes
-must match bit for bit; outputs must not change by a bit when the physical
+would not catch a wrong block or head mapping.  Block tables and fp8 / int8
+codes must match bit for bit; outputs must not change by a bit when the physical
 placement of blocks changes."""
 
 import numpy as np
@@ -73,28 +73,39 @@ def test_fp8_long_context(variant):
     check_decode(w, rows=[0, 7, 15], heads=heads)
 
 
+@pytest.mark.parametrize("variant", ["peaked", "needle"])
+def test_int8_long_context(variant):
+    w = W.int8_long(variant=variant, batch=4, length=65536)
+    heads = list(range(0, 8)) + list(range(56, 64))
+    check_decode(w, rows=[0, 3], heads=heads)
+
+
 EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025, 2047, 4097]
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8", "int8"])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 1), (4, 4), (12, 3)])
 def test_edge_lengths(kv, hq, hkv):
     for variant in ("peaked", "needle"):
         check_decode(W.custom(EDGE, hq, hkv, kv, seed=21, variant=variant))
 
 
-def test_fp8_codes_bit_exact():
-    """The cache write's E4M3 codes equal the oracle codec's, byte for byte."""
+@pytest.mark.parametrize("kv", ["fp8", "int8"])
+def test_one_byte_codes_bit_exact(kv):
+    """The cache write's fp8 (E4M3) and int8 codes equal the oracle codec's,
+    byte for byte, K and V, at every written position."""
     from oracle import fp8 as OF
+    from oracle import int8 as OI
 
-    w = W.custom([37, 300, 1000], 8, 2, "fp8", seed=31)
-    case("fp8 codes")
+    codec = {"fp8": OF, "int8": OI}[kv]
+    w = W.custom([37, 300, 1000], 8, 2, kv, seed=31)
+    case(f"{kv} codes")
     hip = HipSide(w)
     lens, starts = W.replay_lengths(w)
-    kp = hip.cache.k_pool[0].cpu().numpy()  # [NB, hkv, 16, 128]
-    # fp8 V tiles (2 KiB per block and kv head): (d, token) at byte
+    kp = hip.cache.k_pool[0].cpu().view(torch.uint8).numpy()  # [NB, hkv, 16, 128]
+    # one-byte V tiles (2 KiB per block and kv head): (d, token) at byte
     # (token // 4) * 512 + (d % 16) * 32 + (d // 16) * 4 + token % 4
-    vp = hip.cache.v_pool[0].cpu().numpy().reshape(w.num_blocks, w.hkv, 2048)
+    vp = hip.cache.v_pool[0].cpu().view(torch.uint8).numpy().reshape(w.num_blocks, w.hkv, 2048)
     dd = np.arange(128)
     for op in w.script:
         if op.kind != "append":
@@ -107,9 +118,12 @@ def test_fp8_codes_bit_exact():
             gk = kp[blk, j, off, :]
             vidx = (off[:, None] // 4) * 512 + (dd[None, :] % 16) * 32 + (dd[None, :] // 16) * 4 + off[:, None] % 4
             gv = vp[blk[:, None], j, vidx]
-            ok = OF.quantise_scaled(k[:, j].float().cpu().numpy(), w.k_scale[j])
-            ov = OF.quantise_scaled(v[:, j].float().cpu().numpy(), w.v_scale[j])
+            ok = codec.quantise_scaled(k[:, j].float().cpu().numpy(), w.k_scale[j]).view(np.uint8)
+            ov = codec.quantise_scaled(v[:, j].float().cpu().numpy(), w.v_scale[j]).view(np.uint8)
             assert np.array_equal(gk, ok) and np.array_equal(gv, ov)
+    if kv == "int8":  # -128 is never written, and the seeded scales make the clamp at +-127 happen
+        codes = kp.view(np.int8).astype(np.int32)
+        assert (codes != -128).all() and (np.abs(codes) == 127).any()
 
 
 def test_partitions_agree_and_are_deterministic():

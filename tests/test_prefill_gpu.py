@@ -1,5 +1,6 @@
 """GPU parity of chunked prefill batched with decode rows (through the C ABI)
-against the fp64 oracle (max abs error 2e-2 for bf16, 6e-2 for an fp8 cache)."""
+against the fp64 oracle (max abs error 2e-2 for bf16 and int8 caches, 6e-2
+for an fp8 cache)."""
 
 import numpy as np
 import pytest
@@ -39,7 +40,7 @@ SMALL = [(0, 17), (5, 16), (100, 33), (0, 1), (1000, 64), (37, 200), (16, 15)]
 
 
 @pytest.mark.parametrize("variant", ["plain", "peaked"])
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_small_chunks_with_decode_rows(kv, variant):
     check_prefill(W.chunks(SMALL, hq=8, hkv=2, kv_dtype=kv, n_decode=3, variant=variant))
 
@@ -49,11 +50,13 @@ def test_group_sizes(hq, hkv):
     check_prefill(W.chunks([(50, 70), (0, 33)], hq=hq, hkv=hkv, n_decode=2, variant="peaked", seed=13))
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_chunked_1024_over_16k_context_with_32_decodes(kv):
     w = W.chunked(context=16384)
     if kv == "fp8":
         w = W.scaled_fp8(w)
+    elif kv == "int8":
+        w = W.scaled_int8(w)
     w.variant = "peaked"
     toks = [0, 1, 15, 16, 17, 63, 64, 65, 511, 512, 777, 1000, 1022, 1023]
     check_prefill(w, tokens=toks)

@@ -24,6 +24,8 @@ Workloads (shapes from the configurations the benchmarks are quoted on):
                     64 / 8 heads, bf16.
 * ``fp8_long``      16 sequences of 131072 tokens, 64 / 8 heads, bf16 queries,
                     K/V stored as fp8 E4M3 with per-head fp32 scales.
+* ``int8_long``     the same shape with K/V stored as int8 codes with per-head
+                    fp32 scales.
 
 Values: K, V ~ N(0, 1) and Q ~ N(0, 1) ("plain"), or Q ~ N(0, 4^2) ("peaked":
 the softmax concentrates on a few tokens so outputs are O(1)), or plain values
@@ -64,7 +66,7 @@ class Workload:
     hq: int
     hkv: int
     d: int
-    kv_dtype: str  # 'f32' | 'bf16' | 'fp8'
+    kv_dtype: str  # 'f32' | 'bf16' | 'fp8' | 'int8'
     q_dtype: str  # 'f32' | 'bf16'
     num_blocks: int
     placement: np.ndarray  # int32 permutation: order in which blocks are first handed out
@@ -73,7 +75,7 @@ class Workload:
     q_lens: list  # query tokens per batch row (1 = decode)
     seed: int
     variant: str = "plain"
-    # fp8 only: per kv-head fp32 scales for K and V (one layer).
+    # fp8 and int8 only: per kv-head fp32 scales for K and V (one layer).
     k_scale: np.ndarray | None = None
     v_scale: np.ndarray | None = None
     # positions of the tokens each sequence wrote itself: seq -> list of (start, stop)
@@ -224,6 +226,21 @@ def fp8_long(seed: int = 5, variant: str = "plain", batch: int = 16, length: int
                     k_scale=k_scale, v_scale=v_scale, own_ranges=own)
 
 
+def int8_long(seed: int = 6, variant: str = "plain", batch: int = 16, length: int = 131072,
+              hq: int = 64, hkv: int = 8) -> Workload:
+    w = fp8_long(seed, variant, batch, length, hq, hkv)
+    w.name = "int8_long"
+    return scaled_int8(w)
+
+
+def _scaled(w: Workload, kv_dtype: str) -> Workload:
+    if kv_dtype == "fp8":
+        return scaled_fp8(w)
+    if kv_dtype == "int8":
+        return scaled_int8(w)
+    return w
+
+
 def custom(lens, hq: int, hkv: int, kv_dtype: str = "bf16", seed: int = 11, variant: str = "plain",
            pool_factor: float = 1.2, name: str = "custom") -> Workload:
     """Decode rows of the given lengths (edge cases, small parity cases)."""
@@ -236,7 +253,7 @@ def custom(lens, hq: int, hkv: int, kv_dtype: str = "bf16", seed: int = 11, vari
     w = Workload(name, hq, hkv, 128, "f32" if kv_dtype == "f32" else ("bf16" if kv_dtype == "bf16" else "bf16"),
                  "f32" if kv_dtype == "f32" else "bf16", nb, placement(nb, seed), script,
                  list(range(len(lens))), [1] * len(lens), seed, variant, own_ranges=own)
-    return scaled_fp8(w) if kv_dtype == "fp8" else w
+    return _scaled(w, kv_dtype)
 
 
 def chunks(rows, hq: int = 64, hkv: int = 8, kv_dtype: str = "bf16", seed: int = 12, n_decode: int = 0,
@@ -266,7 +283,7 @@ def chunks(rows, hq: int = 64, hkv: int = 8, kv_dtype: str = "bf16", seed: int =
     nb = _pool_size(logical)
     w = Workload("chunks", hq, hkv, 128, "bf16", "bf16", nb, placement(nb, seed), script,
                  list(range(s)), q_lens, seed, variant, own_ranges=own)
-    return scaled_fp8(w) if kv_dtype == "fp8" else w
+    return _scaled(w, kv_dtype)
 
 
 def scaled_fp8(w: Workload) -> Workload:
@@ -275,6 +292,17 @@ def scaled_fp8(w: Workload) -> Workload:
     w.kv_dtype = "fp8"
     w.k_scale = (1.0 / rng.uniform(48.0, 80.0, size=w.hkv)).astype(np.float32)
     w.v_scale = (1.0 / rng.uniform(48.0, 80.0, size=w.hkv)).astype(np.float32)
+    return w
+
+
+def scaled_int8(w: Workload) -> Workload:
+    """Give a bf16 workload int8 storage with seeded per-head scales: 1/24 ..
+    1/32, so N(0, 1) values use most of the code range and the largest ones
+    (beyond 4 to 5.3 standard deviations) reach the clamp at +-127."""
+    rng = np.random.default_rng(w.seed + 78)
+    w.kv_dtype = "int8"
+    w.k_scale = (1.0 / rng.uniform(24.0, 32.0, size=w.hkv)).astype(np.float32)
+    w.v_scale = (1.0 / rng.uniform(24.0, 32.0, size=w.hkv)).astype(np.float32)
     return w
 
 
