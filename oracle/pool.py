@@ -45,6 +45,17 @@ library follows the same documented policy independently):
   [P3] item (g)); ``share_prefix`` shares the first n tokens, n a multiple of
   16 (prefix matching is block aligned, [P2] "Fast answers").
 * ``free`` drops one reference to each block of the sequence, in logical order.
+* Swapping to host memory ([P2] "When it runs out anyway": ship the blocks over
+  PCIe and bring them back; [P3] "M.65 Inference Serving": overflow blocks to
+  CPU memory and reload them).  ``swap_out`` returns the sequence's block ids
+  in logical order (the caller copies those blocks to host memory before any
+  of them is reused) and drops one reference to each, in that order; the
+  sequence keeps its length and holds no blocks while swapped.  ``swap_in``
+  takes ceil(length / 16) blocks off the free list (all or nothing) and
+  returns them in logical order; the caller copies the host copy into them.
+  A swapped sequence cannot be appended to, forked, shared, swapped out again
+  or put in a block table; it can be freed.  Blocks that were shared when the
+  sequence left come back as private copies.
 """
 
 from __future__ import annotations
@@ -87,6 +98,7 @@ class CopyOp:
 class Seq:
     blocks: list = field(default_factory=list)
     length: int = 0
+    swapped: bool = False
 
 
 class PoolModel:
@@ -170,15 +182,21 @@ class PoolModel:
         self.seqs[s] = Seq()
         return s
 
+    def _resident(self, s: int) -> Seq:
+        q = self._seq(s)
+        if q.swapped:
+            raise BadState(f"sequence {s} is swapped out")
+        return q
+
     def seq_len(self, s: int) -> int:
         return self._seq(s).length
 
     def seq_blocks(self, s: int) -> list:
-        return list(self._seq(s).blocks)
+        return list(self._resident(s).blocks)
 
     def append(self, s: int, n: int):
         """Grow sequence ``s`` by ``n`` tokens; returns (slots, copies)."""
-        q = self._seq(s)
+        q = self._resident(s)
         if n < 0:
             raise InvalidArgument("negative token count")
         L = q.length
@@ -206,7 +224,7 @@ class PoolModel:
         return slots, copies
 
     def fork(self, parent: int) -> int:
-        p = self._seq(parent)
+        p = self._resident(parent)
         for b in p.blocks:
             self.ref[b] += 1
         c = self.seq_create()
@@ -215,7 +233,7 @@ class PoolModel:
         return c
 
     def share_prefix(self, src: int, n_tokens: int) -> int:
-        p = self._seq(src)
+        p = self._resident(src)
         if n_tokens < 0 or n_tokens % BLOCK != 0 or n_tokens > p.length:
             raise InvalidArgument("shared prefix must be block aligned and within the source")
         shared = p.blocks[: n_tokens // BLOCK]
@@ -232,11 +250,34 @@ class PoolModel:
             self._decref(b)
         del self.seqs[s]
 
+    def swap_out(self, s: int) -> list:
+        """Block ids of ``s`` in logical order; then one reference dropped from
+        each, and ``s`` swapped out with its length kept."""
+        q = self._resident(s)
+        ids = list(q.blocks)
+        for b in ids:
+            self._decref(b)
+        q.blocks = []
+        q.swapped = True
+        return ids
+
+    def swap_in(self, s: int) -> list:
+        """Fresh blocks for swapped-out ``s`` (all or nothing), in logical order."""
+        q = self._seq(s)
+        if not q.swapped:
+            raise BadState(f"sequence {s} is not swapped out")
+        n = -(-q.length // BLOCK)
+        if len(self.free_stack) < n:
+            raise OutOfBlocks(f"swap in needs {n} blocks, free {len(self.free_stack)}")
+        q.blocks = [self._pop() for _ in range(n)]
+        q.swapped = False
+        return list(q.blocks)
+
     def block_table(self, seq_ids, max_blocks: int):
         """Rows of physical block ids padded with -1, and the lengths."""
         rows, lens = [], []
         for s in seq_ids:
-            q = self._seq(int(s))
+            q = self._resident(int(s))
             if len(q.blocks) > max_blocks:
                 raise InvalidArgument("sequence has more blocks than max_blocks")
             rows.append(list(q.blocks) + [-1] * (max_blocks - len(q.blocks)))
@@ -253,8 +294,10 @@ class PoolModel:
             "refcount_sum": sum(self.ref),
             "cow_count": self.cow_count,
             "num_seqs": len(self.seqs),
-            "tokens": sum(q.length for q in self.seqs.values()),
-            "waste_tokens": sum(len(q.blocks) * BLOCK - q.length for q in self.seqs.values()),
+            "tokens": sum(q.length for q in self.seqs.values() if not q.swapped),
+            "waste_tokens": sum(len(q.blocks) * BLOCK - q.length for q in self.seqs.values() if not q.swapped),
+            "swapped_seqs": sum(1 for q in self.seqs.values() if q.swapped),
+            "swapped_tokens": sum(q.length for q in self.seqs.values() if q.swapped),
         }
 
 

@@ -120,7 +120,8 @@ def test_kv_bytes_closed_forms():
 
 def snapshot(pool):
     return (list(pool.free_stack), list(pool.ref),
-            {s: (list(q.blocks), q.length) for s, q in pool.seqs.items()}, pool.next_seq_id, pool.cow_count)
+            {s: (list(q.blocks), q.length, q.swapped) for s, q in pool.seqs.items()}, pool.next_seq_id,
+            pool.cow_count)
 
 
 def check_invariants(pool, store_ok=True):
@@ -136,7 +137,11 @@ def check_invariants(pool, store_ok=True):
     assert all(pool.ref[b] == 0 for b in pool.free_stack)
     assert len(pool.free_stack) + sum(1 for r in pool.ref if r > 0) == N
     # I3: blocks = ceil(L / 16), so internal waste <= 15 tokens per sequence
+    # (a swapped-out sequence holds no blocks and keeps its length)
     for q in pool.seqs.values():
+        if q.swapped:
+            assert q.blocks == []
+            continue
         assert len(q.blocks) == -(-q.length // 16)
         assert len(q.blocks) * 16 - q.length <= 15
 
@@ -150,6 +155,7 @@ class Shadow:
         self.np = np
         self.store = P.TokenStore(n_blocks, (), np.int64)
         self.streams = {}
+        self.host = {}  # swapped-out sequences' tokens, read through their blocks at swap-out
         self.counter = 0
 
     def on_create(self, s):
@@ -164,9 +170,18 @@ class Shadow:
         self.store.write(slots, vals)
         self.streams[s] += vals
 
+    def on_swap_out(self, pool, s, ids):
+        L = pool.seq_len(s)
+        self.host[s] = list(self.store.gather(ids, L)) if L else []
+
+    def on_swap_in(self, pool, s, ids):
+        L = pool.seq_len(s)
+        slots = [ids[t // 16] * 16 + t % 16 for t in range(L)]
+        self.store.write(slots, self.host.pop(s))
+
     def check(self, pool):
         for s, stream in self.streams.items():
-            if s not in pool.seqs:
+            if s not in pool.seqs or pool.seqs[s].swapped:
                 continue
             row = pool.seq_blocks(s)
             got = list(self.store.gather(row, pool.seq_len(s))) if stream else []
@@ -174,11 +189,25 @@ class Shadow:
 
 
 def random_script_step(pool, shadow, rng):
-    live = list(pool.seqs)
-    kind = rng.choice(["create", "append", "append", "append", "fork", "share", "free"])
+    live = [s for s, q in pool.seqs.items() if not q.swapped]
+    swapped = [s for s, q in pool.seqs.items() if q.swapped]
+    kind = rng.choice(["create", "append", "append", "append", "fork", "share", "free", "swap_out", "swap_in"])
     before = snapshot(pool)
     try:
-        if kind == "create" or not live:
+        if kind == "swap_in" and swapped:
+            s = rng.choice(swapped)
+            ids = pool.swap_in(s)
+            assert len(ids) == -(-pool.seq_len(s) // 16) and all(pool.ref[b] == 1 for b in ids)
+            shadow.on_swap_in(pool, s, ids)
+        elif kind == "swap_out" and live:
+            s = rng.choice(live)
+            refs = {b: pool.ref[b] for b in pool.seq_blocks(s)}
+            ids = pool.swap_out(s)
+            assert ids == list(refs)
+            for b in ids:  # one reference dropped from each block
+                assert pool.ref[b] == refs[b] - 1
+            shadow.on_swap_out(pool, s, ids)
+        elif kind in ("create", "swap_in", "swap_out") or not live:
             s = pool.seq_create()
             shadow.on_create(s)
         elif kind == "append":
@@ -205,9 +234,10 @@ def random_script_step(pool, shadow, rng):
             shadow.streams[c] = list(shadow.streams[p][:n])
             assert pool.seq_blocks(c) == pool.seq_blocks(p)[: n // 16]
         else:
-            s = rng.choice(live)
+            s = rng.choice(live + swapped)
             pool.seq_free(s)
             del shadow.streams[s]
+            shadow.host.pop(s, None)
     except P.OutOfBlocks:
         # I7: an out-of-blocks error leaves every structure as it was
         assert snapshot(pool) == before
@@ -267,6 +297,42 @@ def test_exhaustive_small_scripts():
                 shadow.check(pool)
             n_scripts += 1
     assert n_scripts == sum(len(ops) ** k for k in range(1, 6))
+
+
+def test_swap_hand_worked():
+    """A script worked out by hand from the documented policy: 6 blocks handed
+    out in identity order, a fork sharing both blocks, a swap-out that frees
+    only the unshared block, a swap-in into fresh blocks."""
+    pool = P.PoolModel(6)
+    a = pool.seq_create()
+    pool.append(a, 20)                      # blocks 0, 1 (4 tokens in block 1)
+    b = pool.fork(a)                        # both shared, refcount 2
+    pool.append(b, 1)                       # b copies partial block 1 into block 2
+    assert pool.seq_blocks(b) == [0, 2] and pool.ref == [2, 1, 1, 0, 0, 0]
+    assert pool.swap_out(a) == [0, 1]       # drops a's references: block 1 is free again
+    assert pool.ref == [1, 0, 1, 0, 0, 0] and pool.free_stack == [5, 4, 3, 1]
+    assert pool.seq_len(a) == 20 and pool.stats()["swapped_seqs"] == 1
+    assert pool.stats()["swapped_tokens"] == 20 and pool.stats()["tokens"] == 21
+    for op in (lambda: pool.append(a, 1), lambda: pool.fork(a), lambda: pool.swap_out(a),
+               lambda: pool.seq_blocks(a), lambda: pool.block_table([a], 4), lambda: pool.swap_in(b)):
+        with pytest.raises(P.BadState):
+            op()
+    c = pool.seq_create()
+    pool.append(c, 48)                      # takes 1, 3, 4 (last freed first)
+    assert pool.seq_blocks(c) == [1, 3, 4]
+    with pytest.raises(P.OutOfBlocks):      # a needs 2 blocks, 1 is free: nothing changes
+        before = snapshot(pool)
+        pool.swap_in(a)
+    assert snapshot(pool) == before
+    pool.seq_free(c)                        # pushes 1, 3, 4: free stack [5, 1, 3, 4]
+    assert pool.swap_in(a) == [4, 3]        # private copies, refcount 1
+    assert pool.ref == [1, 0, 1, 1, 1, 0] and pool.seq_blocks(a) == [4, 3]
+    pool.seq_free(a)
+    d = pool.seq_create()
+    pool.append(d, 5)
+    assert pool.swap_out(d) == [3]
+    pool.seq_free(d)                        # a swapped-out sequence can be freed
+    assert pool.stats()["swapped_seqs"] == 0 and pool.free_stack == [5, 1, 4, 3]
 
 
 def test_errors():
