@@ -39,7 +39,7 @@ import torch
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 DTYPE_LABEL = {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "int8": "int8 kv / bf16 q"}
-WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "int8_long", "chunked")
+WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "int8_long", "chunked", "swap")
 
 
 class TimingEvents:
@@ -201,6 +201,73 @@ def run_chunked(args, w, device):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "prefill_kernel"},
         "decode_part_gbs": round(dec_bytes / (dec_ms / 1e3) / 1e9, 1),
+    }
+
+
+def run_swap(args, device):
+    """Swap one 8192-token sequence of a 32-layer, 8-kv-head bf16 cache (the
+    Llama-3-8B shape: 512 blocks, 1.07 GB of K/V) out to pinned host memory and
+    back into other blocks: seq_swap_out + kv_swap_out, then seq_swap_in +
+    kv_swap_in, each timed with HIP events around the copy kernels.  Also
+    times one plain 1.07 GB device-to-host and host-to-device copy of a
+    contiguous buffer (the host link's DMA rate) for comparison.  The pages
+    quote 34 ms for 1.07 GB over PCIe (~31.6 GB/s)."""
+    import paged_kv_cache_263_amd as pk
+
+    layers, hkv, tokens = 32, 8, 8192
+    nblk = tokens // 16
+    pool = pk.kv_pool_create(2 * nblk + 8, None)
+    cache = pk.KVCache("bf16", layers, 2 * nblk + 8, hkv, device, zero=False)
+    g = torch.Generator(device=device).manual_seed(7)
+    cache.k_pool.view(torch.int16).random_(-32768, 32767, generator=g)
+    cache.v_pool.view(torch.int16).random_(-32768, 32767, generator=g)
+    seq = pk.seq_create(pool)
+    pk.seq_append(pool, seq, tokens)
+    slot = pk.kv_swap_block_bytes(cache)
+    total = nblk * slot
+    host = torch.empty(total, dtype=torch.uint8).pin_memory()
+    ev = TimingEvents(args.warmup + args.steps, 4)
+    stream = torch.cuda.current_stream()
+    out_ms, in_ms, host_ms = [], [], []
+    for i in range(args.warmup + args.steps):
+        t0 = time.perf_counter()
+        ids = pk.seq_swap_out(pool, seq)
+        ev.record(i, 0, stream)
+        pk.kv_swap_out(cache, ids, host)
+        ev.record(i, 1, stream)
+        new_ids = pk.seq_swap_in(pool, seq)
+        ev.record(i, 2, stream)
+        pk.kv_swap_in(cache, host, new_ids)
+        ev.record(i, 3, stream)
+        torch.cuda.synchronize()
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+        if i >= args.warmup:
+            out_ms.append(ev.ms(i, 0, 1))
+            in_ms.append(ev.ms(i, 2, 3))
+    # the host link's DMA rate on one contiguous buffer of the same size
+    dev_buf = torch.empty(total, dtype=torch.uint8, device=device)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(2):
+        e0.record()
+        host.copy_(dev_buf, non_blocking=True)
+        e1.record()
+        dev_buf.copy_(host, non_blocking=True)
+        e2.record()
+        torch.cuda.synchronize()
+    d2h, h2d = e0.elapsed_time(e1), e1.elapsed_time(e2)
+    gbs_out = total / (float(np.mean(out_ms)) / 1e3) / 1e9
+    gbs_in = total / (float(np.mean(in_ms)) / 1e3) / 1e9
+    return {
+        "metric": "swap of one 8192-token sequence to pinned host memory and back: GB/s over the host link",
+        "value": round(min(gbs_out, gbs_in), 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(np.mean(host_ms[args.warmup:])), 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap: 32 layers x 8 kv heads x 128 d bf16 cache, one 8192-token sequence "
+                               "(512 blocks)", "bytes": total, "layers": layers, "kv_heads": hkv, "tokens": tokens},
+        "swap_out_ms": round(float(np.mean(out_ms)), 3), "swap_in_ms": round(float(np.mean(in_ms)), 3),
+        "swap_out_gbs": round(gbs_out, 2), "swap_in_gbs": round(gbs_in, 2),
+        "dma_copy_gbs": {"d2h": round(total / (d2h / 1e3) / 1e9, 2), "h2d": round(total / (h2d / 1e3) / 1e9, 2)},
+        "pages_gbs": round(1.07e9 / 34e-3 / 1e9, 2),
     }
 
 
@@ -431,6 +498,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "chunked":
         print(json.dumps(run_chunked(args, build_workload("chunked", args), device)), flush=True)
+        return
+    if args.workload == "swap":
+        print(json.dumps(run_swap(args, device)), flush=True)
         return
     if args.calibrate_copy_mib:
         src = torch.ones(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=device)

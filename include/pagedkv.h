@@ -86,7 +86,9 @@ typedef struct {
     int64_t cow_count;     /* copies planned so far */
     int64_t num_seqs;      /* live sequences */
     int64_t tokens;        /* sum of live sequence lengths */
-    int64_t waste_tokens;  /* sum over live sequences of blocks*16 - length (each <= 15) */
+    int64_t waste_tokens;  /* sum over resident sequences of blocks*16 - length (each <= 15) */
+    int64_t swapped_seqs;  /* live sequences swapped out to host memory */
+    int64_t swapped_tokens;/* their lengths (tokens counts resident sequences only) */
 } pkv_stats;
 
 /* Create a pool of num_blocks blocks (block_size must be 16).  order: host,
@@ -131,10 +133,29 @@ int seq_fork(pkv_pool* pool, int32_t parent, int32_t* out_child);
 /* New sequence sharing the first n_tokens of src; n_tokens must be a multiple
  * of 16 (prefix matching is block aligned, [P2] "Fast answers"). */
 int seq_share_prefix(pkv_pool* pool, int32_t src, int32_t n_tokens, int32_t* out_seq);
-/* Drop one reference to each block of seq, in logical order; seq is gone. */
+/* Drop one reference to each block of seq, in logical order; seq is gone
+ * (a swapped-out sequence holds no blocks and is simply removed). */
 int seq_free(pkv_pool* pool, int32_t seq);
 int seq_len(const pkv_pool* pool, int32_t seq, int32_t* out_len);
 int seq_num_blocks(const pkv_pool* pool, int32_t seq, int32_t* out_n);
+
+/* Swapping a sequence to host memory when blocks run out ([P2] "When it runs
+ * out anyway": ship the blocks over PCIe and bring them back; [P3] "M.65
+ * Inference Serving": overflow blocks to CPU memory, reload them).
+ * seq_swap_out: out_ids host [cap] receives seq's block ids in logical order
+ * (*n_out = ceil(len / 16)); then one reference is dropped from each, in that
+ * order, and seq is swapped out: it keeps its length and holds no blocks.
+ * Copy those blocks to host memory (kv_swap_out) on the stream before any of
+ * them can be written again.  seq_swap_in: takes ceil(len / 16) blocks (all
+ * or nothing: PKV_ERR_OOM changes nothing) and returns them in logical order
+ * in out_ids; copy the host copy into them with kv_swap_in.  A swapped-out
+ * sequence cannot be appended to, forked, shared, swapped out again, counted
+ * by seq_num_blocks or put in a block table (PKV_ERR_STATE); seq_len and
+ * seq_free work.  Blocks that were shared when it left come back as private
+ * copies.  cap smaller than the block count is PKV_ERR_INVALID (nothing
+ * changes). */
+int seq_swap_out(pkv_pool* pool, int32_t seq, int32_t* out_ids, int32_t cap, int32_t* n_out);
+int seq_swap_in(pkv_pool* pool, int32_t seq, int32_t* out_ids, int32_t cap, int32_t* n_out);
 
 /* Block table rows for n sequences: out_table host [n][max_blocks] (physical
  * block ids, padded with -1), out_lens host [n].  A sequence with more than
@@ -258,6 +279,24 @@ int kv_cache_write(const pkv_cache* cache, int32_t layer, int32_t n_tokens, int3
 /* Copy whole blocks (all layers, K and V) for the copy-on-write operations
  * reported by seq_append.  copies: host [n]; enqueued on stream. */
 int kv_copy_blocks(const pkv_cache* cache, const pkv_copy* copies, int32_t n, void* stream);
+
+/* Bytes one block takes in a swap buffer: num_layers * 2 (K, V) *
+ * num_kv_heads * 16 * head_dim * element size. */
+int kv_swap_block_bytes(const pkv_cache* cache, size_t* out_bytes);
+/* Move n whole blocks (all layers, K and V) between the device cache and a
+ * host swap buffer over the host link ([P2] "When it runs out anyway").
+ *   ids:  host [n], block ids (each in range; they need not be distinct for
+ *         kv_swap_out, must be for kv_swap_in)
+ *   host: pinned host memory (hipHostMalloc or torch pin_memory) of n *
+ *         kv_swap_block_bytes; block i occupies bytes [i * B, (i + 1) * B) as
+ *         [layer][K, V][kv head][the cache's own tile bytes].  Memory that is
+ *         not pinned is PKV_ERR_INVALID.
+ * kv_swap_out copies blocks ids[i] -> host slot i; kv_swap_in copies host
+ * slot i -> block ids[i].  Both are kernels on stream that read or write the
+ * host memory directly; the host must not touch the buffer until the stream
+ * has passed them. */
+int kv_swap_out(const pkv_cache* cache, const int32_t* ids, int32_t n, void* host, void* stream);
+int kv_swap_in(const pkv_cache* cache, const void* host, const int32_t* ids, int32_t n, void* stream);
 
 /* Messages. */
 const char* pkv_strerror(int status);

@@ -196,9 +196,9 @@ class PoolModel:
 
     def append(self, s: int, n: int):
         """Grow sequence ``s`` by ``n`` tokens; returns (slots, copies)."""
-        q = self._resident(s)
-        if n < 0:
+        if n < 0:  # a bad argument is reported before the sequence's state
             raise InvalidArgument("negative token count")
+        q = self._resident(s)
         L = q.length
         have = -(-L // BLOCK)
         want = -(-(L + n) // BLOCK)

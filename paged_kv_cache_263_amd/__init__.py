@@ -21,9 +21,10 @@ __all__ = [
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_incref", "kv_pool_free",
     "kv_pool_refcount", "kv_pool_stats", "kv_pool_free_list",
     "seq_create", "seq_append", "seq_append_batch", "seq_fork", "seq_share_prefix", "seq_free",
-    "seq_len", "seq_num_blocks", "block_table_build",
+    "seq_len", "seq_num_blocks", "seq_swap_out", "seq_swap_in", "block_table_build",
     "paged_attn_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
-    "kv_cache_write", "kv_copy_blocks", "pkv_strerror", "pkv_last_error", "pkv_version",
+    "kv_cache_write", "kv_copy_blocks", "kv_swap_block_bytes", "kv_swap_out", "kv_swap_in",
+    "pkv_strerror", "pkv_last_error", "pkv_version",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
@@ -51,7 +52,8 @@ class pkv_stats(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
                 ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
                 ("refcount_sum", ctypes.c_int64), ("cow_count", ctypes.c_int64),
-                ("num_seqs", ctypes.c_int64), ("tokens", ctypes.c_int64), ("waste_tokens", ctypes.c_int64)]
+                ("num_seqs", ctypes.c_int64), ("tokens", ctypes.c_int64), ("waste_tokens", ctypes.c_int64),
+                ("swapped_seqs", ctypes.c_int64), ("swapped_tokens", ctypes.c_int64)]
 
 
 class pkv_cache(ctypes.Structure):
@@ -91,6 +93,8 @@ _SIGNATURES = {
     "seq_free": (ctypes.c_int, [_p, _i32]),
     "seq_len": (ctypes.c_int, [_p, _i32, _pi32]),
     "seq_num_blocks": (ctypes.c_int, [_p, _i32, _pi32]),
+    "seq_swap_out": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32]),
+    "seq_swap_in": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32]),
     "block_table_build": (ctypes.c_int, [_p, _pi32, _i32, _i32, _pi32, _pi32]),
     "paged_attn_workspace_size": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args),
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -99,6 +103,9 @@ _SIGNATURES = {
     "kv_cache_write": (ctypes.c_int, [ctypes.POINTER(pkv_cache), _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32,
                                       _p, _i32, _p, _p]),
     "kv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_copy), _i32, _p]),
+    "kv_swap_block_bytes": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(ctypes.c_size_t)]),
+    "kv_swap_out": (ctypes.c_int, [ctypes.POINTER(pkv_cache), _pi32, _i32, _p, _p]),
+    "kv_swap_in": (ctypes.c_int, [ctypes.POINTER(pkv_cache), _p, _pi32, _i32, _p]),
     "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_int, []),
@@ -275,6 +282,26 @@ def seq_share_prefix(pool: Pool, src: int, n_tokens: int) -> int:
 
 def seq_free(pool: Pool, seq: int) -> None:
     _check(_lib.seq_free(pool.handle, seq))
+
+
+def _swap_ids(fn, pool: Pool, seq: int) -> list:
+    n = ctypes.c_int32()
+    cap = max(1, -(-seq_len(pool, seq) // BLOCK_SIZE))
+    out = (ctypes.c_int32 * cap)()
+    _check(fn(pool.handle, seq, out, cap, ctypes.byref(n)))
+    return list(out[: n.value])
+
+
+def seq_swap_out(pool: Pool, seq: int) -> list:
+    """Swap seq out: its block ids in logical order (copy them to host memory
+    with kv_swap_out before reusing them); seq then holds no blocks."""
+    return _swap_ids(_lib.seq_swap_out, pool, seq)
+
+
+def seq_swap_in(pool: Pool, seq: int) -> list:
+    """Swap seq back in: its fresh block ids in logical order (copy the host
+    copy into them with kv_swap_in)."""
+    return _swap_ids(_lib.seq_swap_in, pool, seq)
 
 
 def seq_len(pool: Pool, seq: int) -> int:
@@ -488,6 +515,33 @@ def kv_cache_write(cache: KVCache, k_new, v_new, slots, layer: int = 0, rows=Non
                                _ptr(k_new), _ptr(v_new), _dev_ptr(slots), _dev_ptr(rows), _dev_ptr(positions),
                                num_rows,
                                _ptr(block_table), max_blocks, _ptr(kv_lens), _stream(stream)))
+
+
+def kv_swap_block_bytes(cache: KVCache) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.kv_swap_block_bytes(ctypes.byref(cache.desc), ctypes.byref(n)))
+    return n.value
+
+
+def _swap_args(cache: KVCache, ids, host):
+    ids = [int(b) for b in ids]
+    need = len(ids) * kv_swap_block_bytes(cache)
+    if host.is_cuda or not host.is_contiguous() or host.numel() * host.element_size() < need:
+        raise PagedKVError(-1, f"host swap buffer must be a contiguous host tensor of at least {need} bytes")
+    return (ctypes.c_int32 * max(1, len(ids)))(*ids), len(ids)
+
+
+def kv_swap_out(cache: KVCache, ids, host, stream=None) -> None:
+    """Copy blocks ids[i] (all layers, K and V) to slot i of the pinned host
+    tensor ``host`` (at least len(ids) * kv_swap_block_bytes bytes)."""
+    arr, n = _swap_args(cache, ids, host)
+    _check(_lib.kv_swap_out(ctypes.byref(cache.desc), arr, n, ctypes.c_void_p(host.data_ptr()), _stream(stream)))
+
+
+def kv_swap_in(cache: KVCache, host, ids, stream=None) -> None:
+    """Copy slot i of the pinned host tensor ``host`` into block ids[i]."""
+    arr, n = _swap_args(cache, ids, host)
+    _check(_lib.kv_swap_in(ctypes.byref(cache.desc), ctypes.c_void_p(host.data_ptr()), arr, n, _stream(stream)))
 
 
 def kv_copy_blocks(cache: KVCache, copies, stream=None) -> None:

@@ -1,5 +1,6 @@
 // Writes into the paged cache: new tokens' K/V to their slots (with fp8 or
-// int8 quantisation on write), and whole-block copies for copy-on-write.
+// int8 quantisation on write), whole-block copies for copy-on-write, and
+// swap copies of whole blocks to and from pinned host memory.
 //
 // A new block is needed every 16 tokens and a token's slot comes from the
 // host allocator ([P3] "PagedAttention block management", item (c)); a
@@ -9,7 +10,9 @@
 // round-to-nearest-even of fp32(x / scale), saturating at +-448.  The int8
 // cache ([P3] "M.65 Inference Serving", quantising the KV cache) stores
 // code = fp32(x / scale) rounded half to even, clamped to +-127.
+#include <algorithm>
 #include <type_traits>
+#include <vector>
 
 #include "device.h"
 #include "internal.h"
@@ -138,6 +141,94 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(const CopyParams p) {
     for (int64_t e = threadIdx.x; e < n; e += blockDim.x) d[e] = s[e];
 }
 
+// Swap copies between the device pools and a pinned host buffer.  A swap
+// slot holds one block: [layer][K, V][the block's bytes of that layer and
+// pool].  blockIdx: x = block of the batch, y = layer, z = 0 (K) / 1 (V).
+constexpr int kSwapBatch = 64;
+struct SwapParams {
+    int32_t ids[kSwapBatch];
+    char* k_pool;
+    char* v_pool;
+    char* host;           // device address of the host buffer's first slot of this batch
+    int64_t block_bytes;  // one (layer, block) of one pool
+    int64_t layer_bytes;  // one layer of one pool
+    int64_t slot_bytes;   // one block in the host buffer: layers * 2 * block_bytes
+};
+
+// Copies block_bytes (a multiple of 4 KiB / 16-byte words) from src to dst,
+// each thread taking every 256th word with four loads in flight before their
+// stores, so that reads across the host link overlap.
+__device__ __forceinline__ void copy_chunk(const u32x4_t* __restrict__ s, u32x4_t* __restrict__ d, int64_t words) {
+    for (int64_t e = threadIdx.x; e < words; e += 4 * blockDim.x) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = e + k * blockDim.x;
+            if (i < words) v[k] = s[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t i = e + k * blockDim.x;
+            if (i < words) d[i] = v[k];
+        }
+    }
+}
+
+template <bool OUT>
+__global__ __launch_bounds__(256) void kv_swap_kernel(const SwapParams p) {
+    char* dev = (blockIdx.z == 0 ? p.k_pool : p.v_pool) + blockIdx.y * p.layer_bytes +
+                static_cast<int64_t>(p.ids[blockIdx.x]) * p.block_bytes;
+    char* host = p.host + blockIdx.x * p.slot_bytes + (2 * blockIdx.y + blockIdx.z) * p.block_bytes;
+    const int64_t words = p.block_bytes / 16;
+    if constexpr (OUT)
+        copy_chunk(reinterpret_cast<const u32x4_t*>(dev), reinterpret_cast<u32x4_t*>(host), words);
+    else
+        copy_chunk(reinterpret_cast<const u32x4_t*>(host), reinterpret_cast<u32x4_t*>(dev), words);
+}
+
+int64_t swap_block_bytes(const pkv_cache* c) {
+    const int64_t elt = c->kv_dtype == PKV_F32 ? 4 : c->kv_dtype == PKV_BF16 ? 2 : 1;
+    return static_cast<int64_t>(c->num_layers) * 2 * c->num_kv_heads * kTile * elt;
+}
+
+template <bool OUT>
+int launch_swap(const pkv_cache* c, const int32_t* ids, int32_t n, const void* host, void* stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (n < 0 || (n > 0 && (!ids || !host))) return fail(PKV_ERR_INVALID, "swap: bad arguments");
+    if (n == 0) return PKV_OK;
+    for (int32_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= c->num_blocks) return fail(PKV_ERR_INVALID, "swap: block id %d out of range", ids[i]);
+    if (!OUT) {
+        std::vector<int32_t> sorted(ids, ids + n);
+        std::sort(sorted.begin(), sorted.end());
+        if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+            return fail(PKV_ERR_INVALID, "kv_swap_in: a block id is listed twice");
+    }
+    void* dev_host = nullptr;
+    if (hipHostGetDevicePointer(&dev_host, const_cast<void*>(host), 0) != hipSuccess || !dev_host) {
+        (void)hipGetLastError();  // clear the error the lookup left
+        return fail(PKV_ERR_INVALID, "swap: the host buffer is not pinned host memory");
+    }
+    const int64_t elt = c->kv_dtype == PKV_F32 ? 4 : c->kv_dtype == PKV_BF16 ? 2 : 1;
+    SwapParams p{};
+    p.k_pool = static_cast<char*>(c->k_pool);
+    p.v_pool = static_cast<char*>(c->v_pool);
+    p.block_bytes = static_cast<int64_t>(c->num_kv_heads) * kTile * elt;
+    p.layer_bytes = p.block_bytes * c->num_blocks;
+    p.slot_bytes = swap_block_bytes(c);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t base = 0; base < n; base += kSwapBatch) {
+        const int32_t k = n - base < kSwapBatch ? n - base : kSwapBatch;
+        for (int32_t i = 0; i < k; ++i) p.ids[i] = ids[base + i];
+        p.host = static_cast<char*>(dev_host) + base * p.slot_bytes;
+        hipLaunchKernelGGL(kv_swap_kernel<OUT>, dim3(k, c->num_layers, 2), dim3(256), 0, s, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "swap launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -189,6 +280,22 @@ int kv_cache_write(const pkv_cache* c, int32_t layer, int32_t n_tokens, int32_t 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_cache_write launch: %s", hipGetErrorString(e));
     return PKV_OK;
+}
+
+int kv_swap_block_bytes(const pkv_cache* c, size_t* out_bytes) {
+    if (!out_bytes) return fail(PKV_ERR_INVALID, "null output");
+    int st = pkv::check_cache(c);
+    if (st) return st;
+    *out_bytes = static_cast<size_t>(pkv::swap_block_bytes(c));
+    return PKV_OK;
+}
+
+int kv_swap_out(const pkv_cache* c, const int32_t* ids, int32_t n, void* host, void* stream) {
+    return pkv::launch_swap<true>(c, ids, n, host, stream);
+}
+
+int kv_swap_in(const pkv_cache* c, const void* host, const int32_t* ids, int32_t n, void* stream) {
+    return pkv::launch_swap<false>(c, ids, n, host, stream);
 }
 
 int kv_copy_blocks(const pkv_cache* c, const pkv_copy* copies, int32_t n, void* stream) {

@@ -28,6 +28,7 @@ struct Sequence {
     std::vector<int32_t> blocks;  // logical block index -> physical block id
     int32_t len = 0;
     bool live = false;
+    bool swapped = false;  // blocks are in host memory; the table is empty
 };
 
 inline int32_t blocks_for(int64_t tokens) { return static_cast<int32_t>((tokens + kBlock - 1) / kBlock); }
@@ -61,6 +62,15 @@ struct pkv_pool {
             return nullptr;
         }
         return &seqs[s];
+    }
+    // A live sequence that holds its blocks (not swapped out).
+    Sequence* resident(int32_t s, int* status) {
+        Sequence* q = find(s, status);
+        if (q && q->swapped) {
+            *status = fail(PKV_ERR_STATE, "sequence %d is swapped out", s);
+            return nullptr;
+        }
+        return q;
     }
     // Blocks one append of n tokens to q will take (new blocks, plus one if the
     // partial tail block is shared and must be copied first).
@@ -191,6 +201,11 @@ int kv_pool_stats(const pkv_pool* p, pkv_stats* s) {
     r.num_seqs = p->live_seqs;
     for (const Sequence& q : p->seqs) {
         if (!q.live) continue;
+        if (q.swapped) {
+            r.swapped_seqs += 1;
+            r.swapped_tokens += q.len;
+            continue;
+        }
         r.tokens += q.len;
         r.waste_tokens += static_cast<int64_t>(q.blocks.size()) * kBlock - q.len;
     }
@@ -217,7 +232,7 @@ int seq_append(pkv_pool* p, int32_t s, int32_t n, int32_t* out_slots, pkv_copy* 
     if (!p || n < 0 || (n > 0 && !out_slots) || !out_copy || !n_copy)
         return fail(PKV_ERR_INVALID, "seq_append: bad arguments");
     int st = PKV_OK;
-    Sequence* q = p->find(s, &st);
+    Sequence* q = p->resident(s, &st);
     if (!q) return st;
     if (static_cast<int64_t>(q->len) + n > static_cast<int64_t>(INT32_MAX) - kBlock)
         return fail(PKV_ERR_INVALID, "seq_append: length overflow");
@@ -239,7 +254,7 @@ int seq_append_batch(pkv_pool* p, const int32_t* seqs, const int32_t* n_tokens, 
     int64_t need = 0, total = 0;
     for (int32_t i = 0; i < n; ++i) {
         int st = PKV_OK;
-        Sequence* q = p->find(seqs[i], &st);
+        Sequence* q = p->resident(seqs[i], &st);
         if (!q) return st;
         if (n_tokens[i] < 0 || static_cast<int64_t>(q->len) + n_tokens[i] > static_cast<int64_t>(INT32_MAX) - kBlock)
             return fail(PKV_ERR_INVALID, "seq_append_batch: bad token count %d", n_tokens[i]);
@@ -264,7 +279,7 @@ int seq_append_batch(pkv_pool* p, const int32_t* seqs, const int32_t* n_tokens, 
 int seq_fork(pkv_pool* p, int32_t parent, int32_t* out_child) {
     if (!p || !out_child) return fail(PKV_ERR_INVALID, "seq_fork: null argument");
     int st = PKV_OK;
-    if (!p->find(parent, &st)) return st;
+    if (!p->resident(parent, &st)) return st;
     const int32_t c = p->new_seq();  // may move the vector: index afresh below
     Sequence& src = p->seqs[parent];
     for (int32_t b : src.blocks) p->ref[b] += 1;
@@ -277,7 +292,7 @@ int seq_fork(pkv_pool* p, int32_t parent, int32_t* out_child) {
 int seq_share_prefix(pkv_pool* p, int32_t src, int32_t n_tokens, int32_t* out_seq) {
     if (!p || !out_seq) return fail(PKV_ERR_INVALID, "seq_share_prefix: null argument");
     int st = PKV_OK;
-    Sequence* q = p->find(src, &st);
+    Sequence* q = p->resident(src, &st);
     if (!q) return st;
     if (n_tokens < 0 || n_tokens % kBlock != 0 || n_tokens > q->len)
         return fail(PKV_ERR_INVALID, "seq_share_prefix: %d tokens is not a block-aligned prefix of %d", n_tokens, q->len);
@@ -301,7 +316,41 @@ int seq_free(pkv_pool* p, int32_t s) {
     q->blocks.shrink_to_fit();
     q->len = 0;
     q->live = false;
+    q->swapped = false;
     p->live_seqs -= 1;
+    return PKV_OK;
+}
+
+int seq_swap_out(pkv_pool* p, int32_t s, int32_t* out_ids, int32_t cap, int32_t* n_out) {
+    if (!p || !n_out || cap < 0 || (cap > 0 && !out_ids)) return fail(PKV_ERR_INVALID, "seq_swap_out: bad arguments");
+    int st = PKV_OK;
+    Sequence* q = p->resident(s, &st);
+    if (!q) return st;
+    const int32_t n = static_cast<int32_t>(q->blocks.size());
+    if (n > cap) return fail(PKV_ERR_INVALID, "seq_swap_out: capacity %d < %d blocks", cap, n);
+    std::copy(q->blocks.begin(), q->blocks.end(), out_ids);
+    for (int32_t b : q->blocks) p->drop(b);
+    q->blocks.clear();
+    q->swapped = true;
+    *n_out = n;
+    return PKV_OK;
+}
+
+int seq_swap_in(pkv_pool* p, int32_t s, int32_t* out_ids, int32_t cap, int32_t* n_out) {
+    if (!p || !n_out || cap < 0 || (cap > 0 && !out_ids)) return fail(PKV_ERR_INVALID, "seq_swap_in: bad arguments");
+    int st = PKV_OK;
+    Sequence* q = p->find(s, &st);
+    if (!q) return st;
+    if (!q->swapped) return fail(PKV_ERR_STATE, "sequence %d is not swapped out", s);
+    const int32_t n = blocks_for(q->len);
+    if (n > cap) return fail(PKV_ERR_INVALID, "seq_swap_in: capacity %d < %d blocks", cap, n);
+    if (static_cast<size_t>(n) > p->free_stack.size())
+        return fail(PKV_ERR_OOM, "seq_swap_in: need %d blocks, %zu free", n, p->free_stack.size());
+    q->blocks.resize(n);
+    for (int32_t j = 0; j < n; ++j) q->blocks[j] = p->take();
+    std::copy(q->blocks.begin(), q->blocks.end(), out_ids);
+    q->swapped = false;
+    *n_out = n;
     return PKV_OK;
 }
 
@@ -317,7 +366,7 @@ int seq_len(const pkv_pool* p, int32_t s, int32_t* out_len) {
 int seq_num_blocks(const pkv_pool* p, int32_t s, int32_t* out_n) {
     if (!p || !out_n) return fail(PKV_ERR_INVALID, "seq_num_blocks: null argument");
     int st = PKV_OK;
-    const Sequence* q = const_cast<pkv_pool*>(p)->find(s, &st);
+    const Sequence* q = const_cast<pkv_pool*>(p)->resident(s, &st);
     if (!q) return st;
     *out_n = static_cast<int32_t>(q->blocks.size());
     return PKV_OK;
@@ -329,7 +378,7 @@ int block_table_build(const pkv_pool* p, const int32_t* seqs, int32_t n, int32_t
         return fail(PKV_ERR_INVALID, "block_table_build: bad arguments");
     for (int32_t i = 0; i < n; ++i) {
         int st = PKV_OK;
-        const Sequence* q = const_cast<pkv_pool*>(p)->find(seqs[i], &st);
+        const Sequence* q = const_cast<pkv_pool*>(p)->resident(seqs[i], &st);
         if (!q) return st;
         if (static_cast<int64_t>(q->blocks.size()) > max_blocks)
             return fail(PKV_ERR_INVALID, "sequence %d has %zu blocks > max_blocks %d", seqs[i], q->blocks.size(), max_blocks);

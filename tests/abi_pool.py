@@ -65,6 +65,12 @@ class AbiPool:
         _wrap(pk.seq_free, self.pool, s)
         self.live.discard(s)
 
+    def swap_out(self, s):
+        return _wrap(pk.seq_swap_out, self.pool, s)
+
+    def swap_in(self, s):
+        return _wrap(pk.seq_swap_in, self.pool, s)
+
     def seq_len(self, s):
         return _wrap(pk.seq_len, self.pool, s)
 

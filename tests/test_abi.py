@@ -56,10 +56,10 @@ def compare(model, abi):
     assert list(abi.ref) == model.ref
     st_m, st_a = model.stats(), abi.stats()
     for k in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks", "refcount_sum", "cow_count",
-              "num_seqs", "tokens", "waste_tokens"):
+              "num_seqs", "tokens", "waste_tokens", "swapped_seqs", "swapped_tokens"):
         assert st_m[k] == st_a[k], k
-    live = sorted(model.seqs)
-    assert live == sorted(abi.live)
+    assert sorted(model.seqs) == sorted(abi.live)
+    live = sorted(s for s, q in model.seqs.items() if not q.swapped)
     if live:
         mb = max(len(model.seq_blocks(s)) for s in live) + 1
         assert abi.block_table(live, mb) == tuple(map(list, model.block_table(live, mb)))
@@ -85,9 +85,16 @@ def test_random_scripts_bit_exact(seed):
     model, abi = OP.PoolModel(n, order=order), AbiPool(n, order=order)
     for i in range(250):
         live = sorted(model.seqs)
-        kind = rng.choice(["create", "append", "append", "append", "fork", "share", "free", "raw", "bad"])
+        kind = rng.choice(["create", "append", "append", "append", "fork", "share", "free", "raw", "bad",
+                           "swap_out", "swap_in"])
         if kind == "create" or not live:
             op = lambda s: s.seq_create()
+        elif kind == "swap_out":
+            q = rng.choice(live)  # may be swapped already: both must refuse alike
+            op = lambda s, q=q: s.swap_out(q)
+        elif kind == "swap_in":
+            q = rng.choice(live)  # may be resident: both must refuse alike
+            op = lambda s, q=q: s.swap_in(q)
         elif kind == "append":
             q, k = rng.choice(live), rng.choice([0, 1, 2, 15, 16, 17, 33])
             op = lambda s, q=q, k=k: s.append(q, k)
