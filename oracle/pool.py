@@ -56,10 +56,42 @@ library follows the same documented policy independently):
   A swapped sequence cannot be appended to, forked, shared, swapped out again
   or put in a block table; it can be freed.  Blocks that were shared when the
   sequence left come back as private copies.
+* Prefix caching with retention ([P1] "PagedAttention ...": hash a shared
+  prefix and reuse its KV blocks; [P2] "Sharing, and what makes a prefix
+  reusable": keep a finished request's cache and match new requests against
+  it, on exact token ids, block-aligned, from the very start; [P2] "The
+  isolation question": key the cache per tenant).  Readings:
+  - A full block (16 tokens) is keyed by a chain: key_j = FNV-1a-64 over the
+    bytes of key_{j-1} (8 bytes little-endian; 0 before the first block), the
+    tenant (4 bytes) and the block's 16 token ids (4 bytes each), all
+    little-endian.  An entry records the key, the block, the parent key, the
+    tenant and the 16 ids; a lookup matches only when all of them agree, so a
+    hash collision cannot produce a wrong match.
+  - ``create_cached(tenant, tokens)`` starts a sequence with as many leading
+    full blocks of ``tokens`` as the cache holds, at most len(tokens) - 1
+    tokens (one token is always left to compute).  A matched block gains a
+    reference; if it was retained with no reference it leaves the evictable
+    list.  The sequence records the tenant and the keys of its blocks.
+  - ``cache_tokens(s, start, tokens)`` registers the sequence's full blocks
+    holding positions start .. start + len - 1; ``start`` must equal 16 x the
+    blocks already keyed (matched or registered), and the positions must be
+    written.  A block whose key is already in the cache (same content keyed
+    earlier by another block) stays unregistered.
+  - A registered block whose last reference drops is retained: it goes to the
+    evictable list (least recently used first) instead of the free stack.
+    When a sequence drops several at once (free, swap-out), the deeper blocks
+    are listed as older, so a chain is evicted from its leaves back to its root.
+  - Taking a block uses the free stack first; when it is empty, the oldest
+    evictable block is reused and its cache entry removed.  Every
+    all-or-nothing check counts free plus evictable blocks.
+  - fork and share_prefix carry the tenant and the keys of the shared blocks.
+    A swapped-out sequence forgets its keys: its blocks come back private and
+    unregistered.
 """
 
 from __future__ import annotations
 
+import struct
 from dataclasses import dataclass, field
 
 BLOCK = 16
@@ -99,6 +131,37 @@ class Seq:
     blocks: list = field(default_factory=list)
     length: int = 0
     swapped: bool = False
+    tenant: int = 0
+    keys: list = field(default_factory=list)  # chain key of each leading keyed block
+
+
+FNV_OFFSET = 0xCBF29CE484222325
+FNV_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes) -> int:
+    """64-bit FNV-1a (Fowler, Noll, Vo): xor each byte in, then multiply."""
+    h = FNV_OFFSET
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def block_key(parent_key: int, tenant: int, token_ids) -> int:
+    """Chain key of one full block (see the module docstring)."""
+    ids = [int(t) for t in token_ids]
+    assert len(ids) == BLOCK
+    data = struct.pack("<QI", parent_key, tenant & 0xFFFFFFFF) + struct.pack(f"<{BLOCK}i", *ids)
+    return fnv1a64(data)
+
+
+@dataclass
+class CacheEntry:
+    block: int
+    parent_key: int
+    tenant: int
+    tokens: tuple
 
 
 class PoolModel:
@@ -121,24 +184,53 @@ class PoolModel:
         self.seqs: dict[int, Seq] = {}
         self.next_seq_id = 0
         self.cow_count = 0
+        self.cache: dict[int, CacheEntry] = {}  # key -> entry
+        self.key_of: dict[int, int] = {}        # registered block -> key
+        self.evictable: list = []               # retained blocks, least recently used first
+        self.matched_tokens = 0
 
     # -- raw blocks -------------------------------------------------------
+    def available(self) -> int:
+        """Blocks a request can take: the free stack plus the evictable list."""
+        return len(self.free_stack) + len(self.evictable)
+
     def _pop(self) -> int:
-        b = self.free_stack.pop()
+        if self.free_stack:
+            b = self.free_stack.pop()
+        else:  # reuse the least recently used retained block; its entry goes
+            b = self.evictable.pop(0)
+            del self.cache[self.key_of.pop(b)]
         assert self.ref[b] == 0
         self.ref[b] = 1
         return b
 
-    def _decref(self, b: int) -> None:
+    def _decref(self, b: int, retained=None) -> None:
+        """Drop one reference; at 0 a registered block is retained (appended
+        to ``retained`` if given, else straight to the evictable list) and any
+        other block goes back on the free stack."""
         self.ref[b] -= 1
         if self.ref[b] == 0:
-            self.free_stack.append(b)
+            if b in self.key_of:
+                if retained is None:
+                    self.evictable.append(b)
+                else:
+                    retained.append(b)
+            else:
+                self.free_stack.append(b)
+
+    def _drop_all(self, blocks) -> None:
+        """Drop one reference from each block in logical order; the ones that
+        become retained join the evictable list deepest first (oldest)."""
+        retained = []
+        for b in blocks:
+            self._decref(b, retained)
+        self.evictable.extend(reversed(retained))
 
     def alloc(self, n: int) -> list:
         if n < 0:
             raise InvalidArgument("negative count")
-        if len(self.free_stack) < n:
-            raise OutOfBlocks(f"need {n}, free {len(self.free_stack)}")
+        if self.available() < n:
+            raise OutOfBlocks(f"need {n}, available {self.available()}")
         return [self._pop() for _ in range(n)]
 
     def _check_ids(self, ids) -> list:
@@ -205,8 +297,8 @@ class PoolModel:
         need = want - have
         if n > 0 and L % BLOCK != 0 and self.ref[q.blocks[L // BLOCK]] > 1:
             need += 1
-        if len(self.free_stack) < need:
-            raise OutOfBlocks(f"append needs {need} blocks, free {len(self.free_stack)}")
+        if self.available() < need:
+            raise OutOfBlocks(f"append needs {need} blocks, available {self.available()}")
         slots, copies = [], []
         for t in range(L, L + n):
             j, o = divmod(t, BLOCK)
@@ -230,6 +322,8 @@ class PoolModel:
         c = self.seq_create()
         self.seqs[c].blocks = list(p.blocks)
         self.seqs[c].length = p.length
+        self.seqs[c].tenant = p.tenant
+        self.seqs[c].keys = list(p.keys)
         return c
 
     def share_prefix(self, src: int, n_tokens: int) -> int:
@@ -242,12 +336,13 @@ class PoolModel:
         c = self.seq_create()
         self.seqs[c].blocks = list(shared)
         self.seqs[c].length = n_tokens
+        self.seqs[c].tenant = p.tenant
+        self.seqs[c].keys = p.keys[: n_tokens // BLOCK]
         return c
 
     def seq_free(self, s: int) -> None:
         q = self._seq(s)
-        for b in q.blocks:
-            self._decref(b)
+        self._drop_all(q.blocks)
         del self.seqs[s]
 
     def swap_out(self, s: int) -> list:
@@ -255,9 +350,9 @@ class PoolModel:
         each, and ``s`` swapped out with its length kept."""
         q = self._resident(s)
         ids = list(q.blocks)
-        for b in ids:
-            self._decref(b)
+        self._drop_all(ids)
         q.blocks = []
+        q.keys = []
         q.swapped = True
         return ids
 
@@ -267,11 +362,58 @@ class PoolModel:
         if not q.swapped:
             raise BadState(f"sequence {s} is not swapped out")
         n = -(-q.length // BLOCK)
-        if len(self.free_stack) < n:
-            raise OutOfBlocks(f"swap in needs {n} blocks, free {len(self.free_stack)}")
+        if self.available() < n:
+            raise OutOfBlocks(f"swap in needs {n} blocks, available {self.available()}")
         q.blocks = [self._pop() for _ in range(n)]
         q.swapped = False
         return list(q.blocks)
+
+    # -- prefix cache ---------------------------------------------------------
+    def create_cached(self, tenant: int, tokens) -> tuple:
+        """New sequence holding the longest cached run of leading full blocks
+        of ``tokens`` (at most len(tokens) - 1 tokens); returns (seq, tokens
+        matched)."""
+        tokens = [int(t) for t in tokens]
+        blocks, keys = [], []
+        parent = 0
+        for j in range(max(0, len(tokens) - 1) // BLOCK):
+            ids = tuple(tokens[BLOCK * j: BLOCK * (j + 1)])
+            key = block_key(parent, tenant, ids)
+            e = self.cache.get(key)
+            if e is None or e.parent_key != parent or e.tenant != tenant or e.tokens != ids:
+                break
+            blocks.append(e.block)
+            keys.append(key)
+            parent = key
+        for b in blocks:
+            if self.ref[b] == 0:
+                self.evictable.remove(b)
+            self.ref[b] += 1
+        s = self.seq_create()
+        q = self.seqs[s]
+        q.blocks, q.keys, q.length, q.tenant = blocks, keys, BLOCK * len(blocks), tenant
+        self.matched_tokens += BLOCK * len(blocks)
+        return s, BLOCK * len(blocks)
+
+    def cache_tokens(self, s: int, start: int, tokens) -> int:
+        """Key and register the full blocks of ``s`` covering positions start
+        .. start + len(tokens) - 1; returns how many blocks were keyed."""
+        q = self._resident(s)
+        tokens = [int(t) for t in tokens]
+        if start != BLOCK * len(q.keys) or start + len(tokens) > q.length:
+            raise InvalidArgument("tokens must start at the first unkeyed block and lie inside the sequence")
+        parent = q.keys[-1] if q.keys else 0
+        n_full = len(tokens) // BLOCK
+        for j in range(n_full):
+            ids = tuple(tokens[BLOCK * j: BLOCK * (j + 1)])
+            key = block_key(parent, q.tenant, ids)
+            b = q.blocks[len(q.keys)]
+            if key not in self.cache and b not in self.key_of:
+                self.cache[key] = CacheEntry(b, parent, q.tenant, ids)
+                self.key_of[b] = key
+            q.keys.append(key)
+            parent = key
+        return n_full
 
     def block_table(self, seq_ids, max_blocks: int):
         """Rows of physical block ids padded with -1, and the lengths."""
@@ -298,6 +440,9 @@ class PoolModel:
             "waste_tokens": sum(len(q.blocks) * BLOCK - q.length for q in self.seqs.values() if not q.swapped),
             "swapped_seqs": sum(1 for q in self.seqs.values() if q.swapped),
             "swapped_tokens": sum(q.length for q in self.seqs.values() if q.swapped),
+            "cached_blocks": len(self.cache),
+            "evictable_blocks": len(self.evictable),
+            "matched_tokens": self.matched_tokens,
         }
 
 
