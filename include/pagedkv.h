@@ -89,6 +89,9 @@ typedef struct {
     int64_t waste_tokens;  /* sum over resident sequences of blocks*16 - length (each <= 15) */
     int64_t swapped_seqs;  /* live sequences swapped out to host memory */
     int64_t swapped_tokens;/* their lengths (tokens counts resident sequences only) */
+    int64_t cached_blocks; /* blocks registered in the prefix cache */
+    int64_t evictable_blocks; /* registered blocks with no reference, kept for reuse */
+    int64_t matched_tokens;/* tokens matched by seq_create_cached so far */
 } pkv_stats;
 
 /* Create a pool of num_blocks blocks (block_size must be 16).  order: host,
@@ -111,6 +114,9 @@ int kv_pool_stats(const pkv_pool* pool, pkv_stats* out);
 /* Copy the free list, bottom to top (the top is handed out next), into
  * out[cap]; *n receives its length (PKV_ERR_INVALID if cap is too small). */
 int kv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+/* Copy the evictable list (retained prefix-cache blocks with no reference),
+ * least recently used first, into out[cap]; *n receives its length. */
+int kv_pool_evictable_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
 
 /* Sequence ids are 0, 1, 2, ... in creation order and are never reused. */
 int seq_create(pkv_pool* pool, int32_t* out_seq);
@@ -156,6 +162,39 @@ int seq_num_blocks(const pkv_pool* pool, int32_t seq, int32_t* out_n);
  * changes). */
 int seq_swap_out(pkv_pool* pool, int32_t seq, int32_t* out_ids, int32_t cap, int32_t* n_out);
 int seq_swap_in(pkv_pool* pool, int32_t seq, int32_t* out_ids, int32_t cap, int32_t* n_out);
+
+/* Prefix caching with retention ([P1] "PagedAttention ...": hash a shared
+ * prefix and reuse its blocks instead of recomputing them; [P2] "Sharing, and
+ * what makes a prefix reusable": a finished request's cache is kept and new
+ * requests match against it on exact token ids, block-aligned, from the very
+ * start; [P2] "The isolation question": key the cache per tenant).
+ *   Keys: full block j of a sequence has key_j = FNV-1a-64 over the
+ *   little-endian bytes of key_{j-1} (8 bytes; 0 for the first block), the
+ *   tenant (4 bytes) and its 16 token ids (4 bytes each).  An entry keeps the
+ *   key, block, parent key, tenant and ids; a match needs all of them equal,
+ *   so a hash collision cannot match wrong content.
+ *   Retention: a registered block whose last reference drops goes to the
+ *   evictable list instead of the free list (a sequence dropping several at
+ *   once lists its deeper blocks as older).  Blocks are taken from the free
+ *   list first, then from the evictable list, least recently used first, which
+ *   removes the block's entry; every all-or-nothing check counts both lists.
+ *   fork and seq_share_prefix carry the tenant and keys of the shared blocks;
+ *   seq_swap_out forgets them (blocks come back private and unregistered).
+ * seq_create_cached: a new sequence of the given tenant holding the longest
+ * run of leading full blocks of tokens[0..n) found in the cache, at most n - 1
+ * tokens (one token is always left to compute); *out_matched receives its
+ * length (a multiple of 16).  Matched blocks gain a reference (and leave the
+ * evictable list).  Append the remaining tokens with seq_append.
+ * seq_cache_tokens: key and register the full blocks of seq covering
+ * positions start .. start + n - 1, whose token ids are tokens[0..n); start
+ * must be 16 x the blocks already keyed (seq_create_cached's *out_matched, then
+ * advancing by 16 x *out_keyed) and the positions must lie inside the sequence
+ * (PKV_ERR_INVALID otherwise).  A block whose key is already registered to
+ * another block stays unregistered.  *out_keyed = n / 16. */
+int seq_create_cached(pkv_pool* pool, int32_t tenant, const int32_t* tokens, int32_t n, int32_t* out_seq,
+                      int32_t* out_matched);
+int seq_cache_tokens(pkv_pool* pool, int32_t seq, int32_t start, const int32_t* tokens, int32_t n,
+                     int32_t* out_keyed);
 
 /* Block table rows for n sequences: out_table host [n][max_blocks] (physical
  * block ids, padded with -1), out_lens host [n].  A sequence with more than

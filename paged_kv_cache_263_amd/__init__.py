@@ -6,7 +6,7 @@ used for device memory and streams; every step of the computation runs in the
 library's host allocator or its HIP kernels.  There is no fallback: if the
 library is missing, importing this package fails.
 
-Build the library with ``python -m paged_kv_cache_263_amd.build``.
+Build the library with ``python paged_kv_cache_263_amd/build.py``.
 """
 
 from __future__ import annotations
@@ -19,9 +19,10 @@ import torch  # imported first: the library then binds to the HIP runtime torch 
 __all__ = [
     "PagedKVError", "Pool", "KVCache", "LIB_PATH",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_incref", "kv_pool_free",
-    "kv_pool_refcount", "kv_pool_stats", "kv_pool_free_list",
+    "kv_pool_refcount", "kv_pool_stats", "kv_pool_free_list", "kv_pool_evictable_list",
     "seq_create", "seq_append", "seq_append_batch", "seq_fork", "seq_share_prefix", "seq_free",
-    "seq_len", "seq_num_blocks", "seq_swap_out", "seq_swap_in", "block_table_build",
+    "seq_len", "seq_num_blocks", "seq_swap_out", "seq_swap_in", "seq_create_cached", "seq_cache_tokens",
+    "block_table_build",
     "paged_attn_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
     "kv_cache_write", "kv_copy_blocks", "kv_swap_block_bytes", "kv_swap_out", "kv_swap_in",
     "pkv_strerror", "pkv_last_error", "pkv_version",
@@ -53,7 +54,9 @@ class pkv_stats(ctypes.Structure):
                 ("used_blocks", ctypes.c_int32), ("shared_blocks", ctypes.c_int32),
                 ("refcount_sum", ctypes.c_int64), ("cow_count", ctypes.c_int64),
                 ("num_seqs", ctypes.c_int64), ("tokens", ctypes.c_int64), ("waste_tokens", ctypes.c_int64),
-                ("swapped_seqs", ctypes.c_int64), ("swapped_tokens", ctypes.c_int64)]
+                ("swapped_seqs", ctypes.c_int64), ("swapped_tokens", ctypes.c_int64),
+                ("cached_blocks", ctypes.c_int64), ("evictable_blocks", ctypes.c_int64),
+                ("matched_tokens", ctypes.c_int64)]
 
 
 class pkv_cache(ctypes.Structure):
@@ -85,6 +88,7 @@ _SIGNATURES = {
     "kv_pool_refcount": (ctypes.c_int, [_p, _i32, _pi32]),
     "kv_pool_stats": (ctypes.c_int, [_p, ctypes.POINTER(pkv_stats)]),
     "kv_pool_free_list": (ctypes.c_int, [_p, _pi32, _i32, _pi32]),
+    "kv_pool_evictable_list": (ctypes.c_int, [_p, _pi32, _i32, _pi32]),
     "seq_create": (ctypes.c_int, [_p, _pi32]),
     "seq_append": (ctypes.c_int, [_p, _i32, _i32, _pi32, ctypes.POINTER(pkv_copy), _pi32]),
     "seq_append_batch": (ctypes.c_int, [_p, _pi32, _pi32, _i32, _pi32, ctypes.POINTER(pkv_copy), _pi32]),
@@ -95,6 +99,8 @@ _SIGNATURES = {
     "seq_num_blocks": (ctypes.c_int, [_p, _i32, _pi32]),
     "seq_swap_out": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32]),
     "seq_swap_in": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32]),
+    "seq_create_cached": (ctypes.c_int, [_p, _i32, _pi32, _i32, _pi32, _pi32]),
+    "seq_cache_tokens": (ctypes.c_int, [_p, _i32, _i32, _pi32, _i32, _pi32]),
     "block_table_build": (ctypes.c_int, [_p, _pi32, _i32, _i32, _pi32, _pi32]),
     "paged_attn_workspace_size": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args),
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -114,7 +120,7 @@ _SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run: python -m paged_kv_cache_263_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run: python paged_kv_cache_263_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
@@ -225,6 +231,33 @@ def kv_pool_free_list(pool: Pool) -> list:
     out = (ctypes.c_int32 * max(1, cap))()
     _check(_lib.kv_pool_free_list(pool.handle, out, cap, ctypes.byref(n)))
     return list(out[: n.value])
+
+
+def kv_pool_evictable_list(pool: Pool) -> list:
+    """Retained prefix-cache blocks with no reference, least recently used first."""
+    n = ctypes.c_int32()
+    cap = kv_pool_stats(pool)["num_blocks"]
+    out = (ctypes.c_int32 * max(1, cap))()
+    _check(_lib.kv_pool_evictable_list(pool.handle, out, cap, ctypes.byref(n)))
+    return list(out[: n.value])
+
+
+def seq_create_cached(pool: Pool, tenant: int, tokens) -> tuple:
+    """New sequence holding the cached leading full blocks of ``tokens``;
+    returns (seq, tokens matched)."""
+    arr, n = _i32_array(tokens)
+    s, m = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.seq_create_cached(pool.handle, tenant, arr, n, ctypes.byref(s), ctypes.byref(m)))
+    return s.value, m.value
+
+
+def seq_cache_tokens(pool: Pool, seq: int, start: int, tokens) -> int:
+    """Register seq's full blocks holding positions start.. (token ids
+    ``tokens``); returns how many blocks were keyed."""
+    arr, n = _i32_array(tokens)
+    k = ctypes.c_int32()
+    _check(_lib.seq_cache_tokens(pool.handle, seq, start, arr, n, ctypes.byref(k)))
+    return k.value
 
 
 def seq_create(pool: Pool) -> int:

@@ -1,6 +1,9 @@
 """Build libpagedkv.so (host allocator + gfx950 kernels + C ABI) in-tree.
 
-    python -m paged_kv_cache_263_amd.build        # or build() from Python
+    python paged_kv_cache_263_amd/build.py        # or build() from Python
+
+(Run it by path: ``python -m`` would import the package, which loads the
+library this script is about to rebuild.)
 
 Every source is compiled with hipcc for gfx950 only.  Packed fp32 arithmetic
 is switched off for device code (ordinary fp32 code is compiled to scalar fp32

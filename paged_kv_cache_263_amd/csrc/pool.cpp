@@ -12,8 +12,18 @@
 // Policy where the pages are silent (documented in pagedkv.h): blocks are
 // first handed out in the caller's order, then last-freed-first; every
 // request is all-or-nothing, so an out-of-blocks error changes nothing.
+//
+// Prefix caching with retention ([P1] "PagedAttention ...": hash a shared
+// prefix and reuse its blocks; [P2] "Sharing, and what makes a prefix
+// reusable": keep a finished request's cache, match new requests on exact
+// token ids, block-aligned, from the start; [P2] "The isolation question": key
+// per tenant).  Full blocks are keyed by an FNV-1a-64 chain over (parent key,
+// tenant, 16 token ids); a registered block whose last reference drops is
+// retained on an LRU list and reused only when the free stack is empty.
 #include <algorithm>
+#include <cstring>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "internal.h"
@@ -28,10 +38,38 @@ struct Sequence {
     std::vector<int32_t> blocks;  // logical block index -> physical block id
     int32_t len = 0;
     bool live = false;
-    bool swapped = false;  // blocks are in host memory; the table is empty
+    bool swapped = false;         // blocks are in host memory; the table is empty
+    int32_t tenant = 0;
+    std::vector<uint64_t> keys;   // chain key of each leading keyed block
 };
 
 inline int32_t blocks_for(int64_t tokens) { return static_cast<int32_t>((tokens + kBlock - 1) / kBlock); }
+
+// 64-bit FNV-1a (Fowler, Noll, Vo) over the little-endian bytes of
+// (parent key, tenant, the block's 16 token ids).
+uint64_t block_key(uint64_t parent, int32_t tenant, const int32_t* ids) {
+    unsigned char buf[8 + 4 + 4 * kBlock];
+    for (int i = 0; i < 8; ++i) buf[i] = static_cast<unsigned char>(parent >> (8 * i));
+    const uint32_t t = static_cast<uint32_t>(tenant);
+    for (int i = 0; i < 4; ++i) buf[8 + i] = static_cast<unsigned char>(t >> (8 * i));
+    for (int k = 0; k < kBlock; ++k) {
+        const uint32_t v = static_cast<uint32_t>(ids[k]);
+        for (int i = 0; i < 4; ++i) buf[12 + 4 * k + i] = static_cast<unsigned char>(v >> (8 * i));
+    }
+    uint64_t h = 0xCBF29CE484222325ull;
+    for (unsigned char c : buf) {
+        h ^= c;
+        h *= 0x100000001B3ull;
+    }
+    return h;
+}
+
+struct CacheEntry {
+    int32_t block;
+    uint64_t parent;
+    int32_t tenant;
+    int32_t ids[kBlock];
+};
 
 }  // namespace
 
@@ -42,15 +80,62 @@ struct pkv_pool {
     std::vector<Sequence> seqs;       // index = sequence id
     int64_t cow_count = 0;
     int64_t live_seqs = 0;
+    // prefix cache
+    std::unordered_map<uint64_t, CacheEntry> cache;  // key -> entry
+    std::vector<uint64_t> key_of;                    // registered block -> its key
+    std::vector<uint8_t> registered;
+    // evictable list (least recently used at the head), linked through the block ids
+    std::vector<int32_t> ev_prev, ev_next;
+    int32_t ev_head = -1, ev_tail = -1;
+    int64_t ev_count = 0;
+    int64_t matched_tokens = 0;
 
+    int64_t available() const { return static_cast<int64_t>(free_stack.size()) + ev_count; }
+    void ev_push_back(int32_t b) {
+        ev_prev[b] = ev_tail;
+        ev_next[b] = -1;
+        if (ev_tail >= 0) ev_next[ev_tail] = b; else ev_head = b;
+        ev_tail = b;
+        ev_count += 1;
+    }
+    void ev_remove(int32_t b) {
+        if (ev_prev[b] >= 0) ev_next[ev_prev[b]] = ev_next[b]; else ev_head = ev_next[b];
+        if (ev_next[b] >= 0) ev_prev[ev_next[b]] = ev_prev[b]; else ev_tail = ev_prev[b];
+        ev_prev[b] = ev_next[b] = -1;
+        ev_count -= 1;
+    }
+    // A block off the free stack, else the least recently used retained block
+    // (its cache entry is removed).  The caller has checked available().
     int32_t take() {
-        int32_t b = free_stack.back();
-        free_stack.pop_back();
+        int32_t b;
+        if (!free_stack.empty()) {
+            b = free_stack.back();
+            free_stack.pop_back();
+        } else {
+            b = ev_head;
+            ev_remove(b);
+            cache.erase(key_of[b]);
+            registered[b] = 0;
+        }
         ref[b] = 1;
         return b;
     }
-    void drop(int32_t b) {
-        if (--ref[b] == 0) free_stack.push_back(b);
+    // Drop one reference; at 0 a registered block is retained (into *retained
+    // if given, else onto the evictable list) and any other block is freed.
+    void drop(int32_t b, std::vector<int32_t>* retained = nullptr) {
+        if (--ref[b] != 0) return;
+        if (registered[b]) {
+            if (retained) retained->push_back(b); else ev_push_back(b);
+        } else {
+            free_stack.push_back(b);
+        }
+    }
+    // Drop one reference from each block in logical order; blocks that become
+    // retained join the evictable list deepest first (evicted first).
+    void drop_all(const std::vector<int32_t>& blocks) {
+        std::vector<int32_t> retained;
+        for (int32_t b : blocks) drop(b, &retained);
+        for (auto it = retained.rbegin(); it != retained.rend(); ++it) ev_push_back(*it);
     }
     Sequence* find(int32_t s, int* status) {
         if (s < 0 || s >= static_cast<int32_t>(seqs.size())) {
@@ -120,6 +205,10 @@ int kv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
     if (!p) return fail(PKV_ERR_INVALID, "host allocation failed");
     p->num_blocks = num_blocks;
     p->ref.assign(num_blocks, 0);
+    p->key_of.assign(num_blocks, 0);
+    p->registered.assign(num_blocks, 0);
+    p->ev_prev.assign(num_blocks, -1);
+    p->ev_next.assign(num_blocks, -1);
     p->free_stack.resize(num_blocks);
     if (order) {
         std::vector<char> seen(num_blocks, 0);
@@ -143,8 +232,8 @@ void kv_pool_destroy(pkv_pool* pool) { delete pool; }
 
 int kv_pool_alloc(pkv_pool* p, int32_t n, int32_t* out_ids) {
     if (!p || n < 0 || (n > 0 && !out_ids)) return fail(PKV_ERR_INVALID, "kv_pool_alloc: bad arguments");
-    if (static_cast<size_t>(n) > p->free_stack.size())
-        return fail(PKV_ERR_OOM, "kv_pool_alloc: need %d blocks, %zu free", n, p->free_stack.size());
+    if (n > p->available())
+        return fail(PKV_ERR_OOM, "kv_pool_alloc: need %d blocks, %lld available", n, static_cast<long long>(p->available()));
     for (int32_t i = 0; i < n; ++i) out_ids[i] = p->take();
     return PKV_OK;
 }
@@ -199,6 +288,9 @@ int kv_pool_stats(const pkv_pool* p, pkv_stats* s) {
     }
     r.cow_count = p->cow_count;
     r.num_seqs = p->live_seqs;
+    r.cached_blocks = static_cast<int64_t>(p->cache.size());
+    r.evictable_blocks = p->ev_count;
+    r.matched_tokens = p->matched_tokens;
     for (const Sequence& q : p->seqs) {
         if (!q.live) continue;
         if (q.swapped) {
@@ -221,6 +313,15 @@ int kv_pool_free_list(const pkv_pool* p, int32_t* out, int32_t cap, int32_t* n) 
     return PKV_OK;
 }
 
+int kv_pool_evictable_list(const pkv_pool* p, int32_t* out, int32_t cap, int32_t* n) {
+    if (!p || !n || cap < 0 || (cap > 0 && !out)) return fail(PKV_ERR_INVALID, "kv_pool_evictable_list: bad arguments");
+    *n = static_cast<int32_t>(p->ev_count);
+    if (*n > cap) return fail(PKV_ERR_INVALID, "kv_pool_evictable_list: capacity %d < %d", cap, *n);
+    int32_t i = 0;
+    for (int32_t b = p->ev_head; b >= 0; b = p->ev_next[b]) out[i++] = b;
+    return PKV_OK;
+}
+
 int seq_create(pkv_pool* p, int32_t* out_seq) {
     if (!p || !out_seq) return fail(PKV_ERR_INVALID, "seq_create: null argument");
     if (p->seqs.size() >= static_cast<size_t>(INT32_MAX)) return fail(PKV_ERR_INVALID, "too many sequences");
@@ -237,8 +338,9 @@ int seq_append(pkv_pool* p, int32_t s, int32_t n, int32_t* out_slots, pkv_copy* 
     if (static_cast<int64_t>(q->len) + n > static_cast<int64_t>(INT32_MAX) - kBlock)
         return fail(PKV_ERR_INVALID, "seq_append: length overflow");
     const int64_t need = p->blocks_needed(*q, n);
-    if (need > static_cast<int64_t>(p->free_stack.size()))
-        return fail(PKV_ERR_OOM, "seq_append: need %lld blocks, %zu free", static_cast<long long>(need), p->free_stack.size());
+    if (need > p->available())
+        return fail(PKV_ERR_OOM, "seq_append: need %lld blocks, %lld available", static_cast<long long>(need),
+                    static_cast<long long>(p->available()));
     p->do_append(*q, n, out_slots, out_copy, n_copy);
     return PKV_OK;
 }
@@ -262,9 +364,9 @@ int seq_append_batch(pkv_pool* p, const int32_t* seqs, const int32_t* n_tokens, 
         total += n_tokens[i];
     }
     if (total > 0 && !out_slots) return fail(PKV_ERR_INVALID, "seq_append_batch: null slots");
-    if (need > static_cast<int64_t>(p->free_stack.size()))
-        return fail(PKV_ERR_OOM, "seq_append_batch: need %lld blocks, %zu free", static_cast<long long>(need),
-                    p->free_stack.size());
+    if (need > p->available())
+        return fail(PKV_ERR_OOM, "seq_append_batch: need %lld blocks, %lld available", static_cast<long long>(need),
+                    static_cast<long long>(p->available()));
     int64_t off = 0;
     *n_copies = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -285,6 +387,8 @@ int seq_fork(pkv_pool* p, int32_t parent, int32_t* out_child) {
     for (int32_t b : src.blocks) p->ref[b] += 1;
     p->seqs[c].blocks = src.blocks;
     p->seqs[c].len = src.len;
+    p->seqs[c].tenant = src.tenant;
+    p->seqs[c].keys = src.keys;
     *out_child = c;
     return PKV_OK;
 }
@@ -302,6 +406,8 @@ int seq_share_prefix(pkv_pool* p, int32_t src, int32_t n_tokens, int32_t* out_se
     p->seqs[c].blocks.assign(s.blocks.begin(), s.blocks.begin() + nb);
     for (int32_t i = 0; i < nb; ++i) p->ref[s.blocks[i]] += 1;
     p->seqs[c].len = n_tokens;
+    p->seqs[c].tenant = s.tenant;
+    p->seqs[c].keys.assign(s.keys.begin(), s.keys.begin() + std::min<size_t>(nb, s.keys.size()));
     *out_seq = c;
     return PKV_OK;
 }
@@ -311,9 +417,11 @@ int seq_free(pkv_pool* p, int32_t s) {
     int st = PKV_OK;
     Sequence* q = p->find(s, &st);
     if (!q) return st;
-    for (int32_t b : q->blocks) p->drop(b);
+    p->drop_all(q->blocks);
     q->blocks.clear();
     q->blocks.shrink_to_fit();
+    q->keys.clear();
+    q->keys.shrink_to_fit();
     q->len = 0;
     q->live = false;
     q->swapped = false;
@@ -329,8 +437,9 @@ int seq_swap_out(pkv_pool* p, int32_t s, int32_t* out_ids, int32_t cap, int32_t*
     const int32_t n = static_cast<int32_t>(q->blocks.size());
     if (n > cap) return fail(PKV_ERR_INVALID, "seq_swap_out: capacity %d < %d blocks", cap, n);
     std::copy(q->blocks.begin(), q->blocks.end(), out_ids);
-    for (int32_t b : q->blocks) p->drop(b);
+    p->drop_all(q->blocks);
     q->blocks.clear();
+    q->keys.clear();
     q->swapped = true;
     *n_out = n;
     return PKV_OK;
@@ -344,13 +453,81 @@ int seq_swap_in(pkv_pool* p, int32_t s, int32_t* out_ids, int32_t cap, int32_t* 
     if (!q->swapped) return fail(PKV_ERR_STATE, "sequence %d is not swapped out", s);
     const int32_t n = blocks_for(q->len);
     if (n > cap) return fail(PKV_ERR_INVALID, "seq_swap_in: capacity %d < %d blocks", cap, n);
-    if (static_cast<size_t>(n) > p->free_stack.size())
-        return fail(PKV_ERR_OOM, "seq_swap_in: need %d blocks, %zu free", n, p->free_stack.size());
+    if (n > p->available())
+        return fail(PKV_ERR_OOM, "seq_swap_in: need %d blocks, %lld available", n, static_cast<long long>(p->available()));
     q->blocks.resize(n);
     for (int32_t j = 0; j < n; ++j) q->blocks[j] = p->take();
     std::copy(q->blocks.begin(), q->blocks.end(), out_ids);
     q->swapped = false;
     *n_out = n;
+    return PKV_OK;
+}
+
+int seq_create_cached(pkv_pool* p, int32_t tenant, const int32_t* tokens, int32_t n, int32_t* out_seq,
+                      int32_t* out_matched) {
+    if (!p || !out_seq || !out_matched || n < 0 || (n > 0 && !tokens))
+        return fail(PKV_ERR_INVALID, "seq_create_cached: bad arguments");
+    if (p->seqs.size() >= static_cast<size_t>(INT32_MAX)) return fail(PKV_ERR_INVALID, "too many sequences");
+    std::vector<int32_t> blocks;
+    std::vector<uint64_t> keys;
+    uint64_t parent = 0;
+    const int32_t max_blocks = n > 0 ? (n - 1) / kBlock : 0;  // one token is always left to compute
+    for (int32_t j = 0; j < max_blocks; ++j) {
+        const int32_t* ids = tokens + static_cast<int64_t>(j) * kBlock;
+        const uint64_t key = block_key(parent, tenant, ids);
+        auto it = p->cache.find(key);
+        if (it == p->cache.end()) break;
+        const CacheEntry& e = it->second;
+        if (e.parent != parent || e.tenant != tenant || std::memcmp(e.ids, ids, sizeof(e.ids)) != 0) break;
+        blocks.push_back(e.block);
+        keys.push_back(key);
+        parent = key;
+    }
+    for (int32_t b : blocks) {
+        if (p->ref[b] == 0) p->ev_remove(b);
+        p->ref[b] += 1;
+    }
+    const int32_t s = p->new_seq();
+    Sequence& q = p->seqs[s];
+    q.len = static_cast<int32_t>(blocks.size()) * kBlock;
+    q.blocks = std::move(blocks);
+    q.keys = std::move(keys);
+    q.tenant = tenant;
+    p->matched_tokens += q.len;
+    *out_seq = s;
+    *out_matched = q.len;
+    return PKV_OK;
+}
+
+int seq_cache_tokens(pkv_pool* p, int32_t s, int32_t start, const int32_t* tokens, int32_t n, int32_t* out_keyed) {
+    if (!p || !out_keyed || n < 0 || (n > 0 && !tokens)) return fail(PKV_ERR_INVALID, "seq_cache_tokens: bad arguments");
+    int st = PKV_OK;
+    Sequence* q = p->resident(s, &st);
+    if (!q) return st;
+    if (static_cast<int64_t>(start) != static_cast<int64_t>(q->keys.size()) * kBlock ||
+        static_cast<int64_t>(start) + n > q->len)
+        return fail(PKV_ERR_INVALID, "seq_cache_tokens: tokens must start at position %zu (the first unkeyed block) "
+                    "and lie inside the sequence's %d tokens", q->keys.size() * kBlock, q->len);
+    uint64_t parent = q->keys.empty() ? 0 : q->keys.back();
+    const int32_t n_full = n / kBlock;
+    for (int32_t j = 0; j < n_full; ++j) {
+        const int32_t* ids = tokens + static_cast<int64_t>(j) * kBlock;
+        const uint64_t key = block_key(parent, q->tenant, ids);
+        const int32_t b = q->blocks[q->keys.size()];
+        if (!p->registered[b] && p->cache.find(key) == p->cache.end()) {
+            CacheEntry e;
+            e.block = b;
+            e.parent = parent;
+            e.tenant = q->tenant;
+            std::memcpy(e.ids, ids, sizeof(e.ids));
+            p->cache.emplace(key, e);
+            p->key_of[b] = key;
+            p->registered[b] = 1;
+        }
+        q->keys.push_back(key);
+        parent = key;
+    }
+    *out_keyed = n_full;
     return PKV_OK;
 }
 

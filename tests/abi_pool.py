@@ -42,6 +42,10 @@ class AbiPool:
     def free_stack(self):
         return pk.kv_pool_free_list(self.pool)
 
+    @property
+    def evictable(self):
+        return pk.kv_pool_evictable_list(self.pool)
+
     def seq_create(self):
         s = _wrap(pk.seq_create, self.pool)
         self.live.add(s)
@@ -70,6 +74,14 @@ class AbiPool:
 
     def swap_in(self, s):
         return _wrap(pk.seq_swap_in, self.pool, s)
+
+    def create_cached(self, tenant, tokens):
+        s, m = _wrap(pk.seq_create_cached, self.pool, tenant, tokens)
+        self.live.add(s)
+        return s, m
+
+    def cache_tokens(self, s, start, tokens):
+        return _wrap(pk.seq_cache_tokens, self.pool, s, start, tokens)
 
     def seq_len(self, s):
         return _wrap(pk.seq_len, self.pool, s)

@@ -53,10 +53,12 @@ def test_golden_scripts_through_the_abi():
 
 def compare(model, abi):
     assert abi.free_stack == model.free_stack
+    assert abi.evictable == model.evictable
     assert list(abi.ref) == model.ref
     st_m, st_a = model.stats(), abi.stats()
     for k in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks", "refcount_sum", "cow_count",
-              "num_seqs", "tokens", "waste_tokens", "swapped_seqs", "swapped_tokens"):
+              "num_seqs", "tokens", "waste_tokens", "swapped_seqs", "swapped_tokens", "cached_blocks",
+              "evictable_blocks", "matched_tokens"):
         assert st_m[k] == st_a[k], k
     assert sorted(model.seqs) == sorted(abi.live)
     live = sorted(s for s, q in model.seqs.items() if not q.swapped)
@@ -116,6 +118,59 @@ def test_random_scripts_bit_exact(seed):
             op = lambda s, q=q: s.append(q, -1)
         step_both(model, abi, op, (i, kind))
         compare(model, abi)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_cache_streams_bit_exact(seed):
+    """Request streams with shared beginnings through both allocators:
+    matches, registrations, retention, LRU reuse, swaps and errors agree op
+    for op."""
+    from test_oracle_prefix_cache import Traffic
+
+    rng = random.Random(2000 + seed)
+    n = rng.choice([16, 32, 96])
+    order = rng.sample(range(n), n)
+    model, abi = OP.PoolModel(n, order=order), AbiPool(n, order=order)
+    traffic = Traffic(rng)
+    for i in range(300):
+        resident = sorted(s for s, q in model.seqs.items() if not q.swapped)
+        kind = rng.choice(["request", "request", "decode", "register", "free", "free", "free", "fork", "swap",
+                           "badstart"])
+        if kind == "request" or not resident:
+            tenant, prompt = rng.choice([1, 2]), traffic.prompt()
+
+            def op(side, tenant=tenant, prompt=prompt):
+                s, m = side.create_cached(tenant, prompt)
+                out = [s, m]
+                try:
+                    out.append(side.append(s, len(prompt) - m)[0])
+                    out.append(side.cache_tokens(s, m, prompt[m:]))
+                except OP.OutOfBlocks:
+                    out.append("oom")
+                return out
+        elif kind == "decode":
+            q, k = rng.choice(resident), rng.choice([1, 5, 16])
+            op = lambda side, q=q, k=k: side.append(q, k)
+        elif kind == "register":
+            q = rng.choice(resident)
+            k = 16 * len(model.seqs[q].keys)
+            toks = [rng.randrange(1000) for _ in range(model.seqs[q].length - k)]
+            op = lambda side, q=q, k=k, toks=toks: side.cache_tokens(q, k, toks)
+        elif kind == "badstart":
+            q = rng.choice(resident)
+            op = lambda side, q=q: side.cache_tokens(q, 16 * len(model.seqs[q].keys) + 16, [1] * 16)
+        elif kind == "fork":
+            q = rng.choice(resident)
+            op = lambda side, q=q: side.fork(q)
+        elif kind == "swap":
+            q = rng.choice(resident)
+            op = lambda side, q=q: (side.swap_out(q), side.swap_in(q))
+        else:
+            q = rng.choice(sorted(model.seqs))
+            op = lambda side, q=q: side.seq_free(q)
+        step_both(model, abi, op, (i, kind))
+        compare(model, abi)
+    assert model.stats()["matched_tokens"] > 0
 
 
 def test_exhaustive_small_scripts_bit_exact():

@@ -67,11 +67,11 @@ class Traffic:
 
     def __init__(self, rng):
         self.rng = rng
-        self.families = [[rng.randrange(1000) for _ in range(rng.choice([8, 16, 40, 64]))] for _ in range(4)]
+        self.families = [[rng.randrange(1000) for _ in range(n)] for n in (8, 40, 64, 100)]
 
     def prompt(self):
         fam = self.rng.choice(self.families)
-        cut = self.rng.randrange(len(fam) + 1)
+        cut = len(fam) if self.rng.random() < 0.5 else self.rng.randrange(len(fam) + 1)
         return fam[:cut] + [self.rng.randrange(1000) for _ in range(self.rng.choice([1, 5, 16, 30]))]
 
 
