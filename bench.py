@@ -39,7 +39,7 @@ import torch
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 DTYPE_LABEL = {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv / bf16 q", "int8": "int8 kv / bf16 q"}
-WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "int8_long", "chunked", "swap")
+WORKLOADS = ("llama8b", "shared_prefix", "fp8_long", "int8_long", "chunked", "swap", "prefix_cache")
 
 
 class TimingEvents:
@@ -201,6 +201,57 @@ def run_chunked(args, w, device):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "prefill_kernel"},
         "decode_part_gbs": round(dec_bytes / (dec_ms / 1e3) / 1e9, 1),
+    }
+
+
+def run_prefix_cache(args):
+    """Serves the four reuse structures of the pages' table (few-shot, agent
+    loop, multi-turn chat, RAG; seeded synthetic token ids) through the
+    library's allocator with prefix caching: match, append the rest, register,
+    append and register the reply, free (blocks retained).  Reports the hit
+    rate (matched / prompt tokens), the prefill tokens saved, and the
+    allocator's request rate on the host."""
+    import paged_kv_cache_263_amd as pk
+    from workloads import traffic as T
+
+    pages = {"few_shot": "95%", "agent": "~90%", "chat": "90%+ by turn 6-8", "rag": "5-15%"}
+    streams = {}
+    t_all, n_all = 0.0, 0
+    for name, make in T.STREAMS.items():
+        reqs = make()
+        pool = pk.kv_pool_create(200000, None)
+        matched = []
+        t0 = time.perf_counter()
+        for r in reqs:
+            s, m = pk.seq_create_cached(pool, 1, r.prompt)
+            pk.seq_append(pool, s, len(r.prompt) - m)
+            keyed = m // 16 + pk.seq_cache_tokens(pool, s, m, r.prompt[m:])
+            if r.reply:
+                full = r.prompt + r.reply
+                pk.seq_append(pool, s, len(r.reply))
+                pk.seq_cache_tokens(pool, s, 16 * keyed, full[16 * keyed:])
+            pk.seq_free(pool, s)
+            matched.append(m)
+        t_all += time.perf_counter() - t0
+        n_all += len(reqs)
+        prompt = sum(len(r.prompt) for r in reqs)
+        entry = {"requests": len(reqs), "prompt_tokens": prompt, "matched_tokens": sum(matched),
+                 "hit_rate": round(sum(matched) / prompt, 4), "pages": pages[name]}
+        if name == "chat":
+            k = max(r.session for r in reqs) + 1
+            entry["hit_rate_by_turn"] = [
+                round(sum(matched[t * k:(t + 1) * k]) / sum(len(r.prompt) for r in reqs[t * k:(t + 1) * k]), 4)
+                for t in range(len(reqs) // k)]
+        streams[name] = entry
+    total_prompt = sum(e["prompt_tokens"] for e in streams.values())
+    total_matched = sum(e["matched_tokens"] for e in streams.values())
+    return {
+        "metric": "prefix caching with retention: prompt tokens matched (prefill saved), pages' reuse structures",
+        "value": round(total_matched / total_prompt, 4), "unit": "fraction of prompt tokens",
+        "n_gpus": 0, "steps": 1, "warmup": 0, "ms_per_step": round(t_all * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32 token ids", "data": "synthetic",
+        "config": {"workload": "few-shot / agent / chat / RAG request streams, 16-token blocks, one tenant"},
+        "streams": streams, "requests_per_s_host": round(n_all / t_all, 1),
     }
 
 
@@ -489,6 +540,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU: the paged decode path has no multi-GPU "
                                    "mode (no sharding or collectives); run with --gpus 1"}))
         sys.exit(2)
+    if args.workload == "prefix_cache":  # host allocator only
+        print(json.dumps(run_prefix_cache(args)), flush=True)
+        return
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
