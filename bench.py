@@ -105,6 +105,8 @@ def parse():
                     help="llama8b: every row this long instead of uniform 512..8192 (a balance control)")
     ap.add_argument("--placement", default="shuffled", choices=("shuffled", "identity"),
                     help="physical block order: the workload's seeded shuffle, or identity (a contiguous control)")
+    ap.add_argument("--no-prefix-pass", action="store_true",
+                    help="shared_prefix: do not pass the shared-prefix promise (every row reads the prefix itself)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -587,7 +589,10 @@ def main():
     h_io = torch.empty((total, 2, B), dtype=torch.int32).pin_memory()
     ones = [1] * B
     # workspace sized for the longest row the run reaches
+    # shared_prefix: every table starts with the prefix's blocks (125 for 2000 tokens)
+    spb = w.shared_prefix_tokens // 16 if (w.name == "shared_prefix" and not args.no_prefix_pass) else 0
     a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.decode_parts, None)
+    a.shared_prefix_blocks = spb
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream()
     ev = TimingEvents(total, 4)
@@ -612,7 +617,8 @@ def main():
         pk.kv_cache_write(cache, k_new[i], v_new[i], h_io[i, 0], rows=d_rows, positions=h_io[i, 1],
                           block_table=d_table, kv_lens=d_lens)
         pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, decode_parts=args.decode_parts,
-                             workspace=ws, events=ev.handles(i, (1, 2, 3) if breakdown else (1, 2)))
+                             workspace=ws, events=ev.handles(i, (1, 2, 3) if breakdown else (1, 2)),
+                             shared_prefix_blocks=spb)
         kv_bytes_step.append(int(lens.sum()) * w.hkv * w.d * 2 * elt_bytes(w))
 
     for i in range(args.warmup):
@@ -659,7 +665,7 @@ def main():
         "config": {"workload": describe(w), "batch": B, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "block_size": 16, "mean_kv_len": round(float(np.mean(lens)), 1),
                    "pool_blocks": w.num_blocks, "decode_parts": args.decode_parts or "auto",
-                   "placement": args.placement},
+                   "placement": args.placement, "shared_prefix_blocks": spb},
         "seq_tokens_per_s": round(tokens_per_s, 1),
         "kernels_us": {"decode": us(split_ms), "decode_merge_warmup": us(merge_ms),
                        "cache_write_warmup": us(write_ms)},

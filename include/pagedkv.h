@@ -257,13 +257,20 @@ typedef struct {
                                     many wavefronts (<= 4096, and at most one per 8 blocks of the
                                     head's work); 0 = auto (8 per compute unit in all, 12 for a
                                     one-byte cache) */
+    int32_t shared_prefix_blocks;/* decode only: the caller promises that the first
+                                    shared_prefix_blocks entries of every row's block table are the
+                                    same block ids (a prefix all rows share); the call then computes
+                                    attention over those blocks once for all rows and continues each
+                                    row from there.  Each row's kv_lens must be at least 16 times
+                                    this (else the row is invalid).  0 = no promise. */
     void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
      * the call records on its stream: [0] just before the decode kernel (after
-     * the plan kernel that batches of more than 1024 rows need), [1] after the
-     * decode kernel, [2] after the decode merge kernel, [3] after the prefill
-     * kernel.  The caller owns the events. */
+     * the plan kernel that batches of more than 1024 rows need; before the
+     * shared-prefix pass, if any), [1] after the decode kernel, [2] after the
+     * decode merge kernel, [3] after the prefill kernel.  The caller owns the
+     * events. */
     void* events[4];
 } pkv_attn_args;
 
@@ -281,6 +288,14 @@ int paged_attn_workspace_size(const pkv_cache* cache, const pkv_attn_args* args,
  * depends on logical positions only, so any placement of the blocks gives
  * bit-identical output.  A row with an invalid length or an out-of-range
  * block id gets NaN output. */
+/* With shared_prefix_blocks = S > 0 (the rows' tables all start with the same
+ * S block ids: a shared prefix, [P2] "Sharing, and what makes a prefix
+ * reusable"), the call first computes, on the matrix cores, every row's
+ * attention state (running max, normaliser, unnormalised output) over the
+ * 16 S prefix tokens, reading those blocks once per kv head instead of once per
+ * row, then runs the decode over each row's remaining blocks starting from
+ * that state.  The result is the same attention (a different summation
+ * order); it is still independent of where the blocks sit. */
 int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
 /* Chunked prefill batched with decode rows ([P1] "Serving systems: the layer

@@ -74,6 +74,7 @@ class pkv_attn_args(ctypes.Structure):
                 ("cu_q", ctypes.c_void_p), ("num_decode", ctypes.c_int32),
                 ("max_decode_kv_len", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("total_q", ctypes.c_int32), ("decode_parts", ctypes.c_int32),
+                ("shared_prefix_blocks", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("events", ctypes.c_void_p * 4)]
 
@@ -498,12 +499,16 @@ def _set_events(a, events):
 
 
 def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, out=None, layer: int = 0,
-                      decode_parts: int = 0, workspace=None, stream=None, events=None):
+                      decode_parts: int = 0, workspace=None, stream=None, events=None,
+                      shared_prefix_blocks: int = 0):
     """q [rows, Hq, 128] -> out [rows, Hq, 128] (q's dtype).  ``events``: up to
-    four hipEvent_t handles (ints) recorded around the kernels (see the header)."""
+    four hipEvent_t handles (ints) recorded around the kernels (see the header).
+    ``shared_prefix_blocks``: the caller's promise that every row's table starts
+    with the same that many block ids (attention over them is computed once)."""
     if out is None:
         out = torch.empty_like(q)
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace)
+    a.shared_prefix_blocks = shared_prefix_blocks
     _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841 (alive until enqueued)
     _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))

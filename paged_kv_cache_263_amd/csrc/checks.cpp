@@ -34,6 +34,12 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
     if (a->num_q_heads / c->num_kv_heads > 16)
         return fail(PKV_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
     if (a->num_seqs < 0) return fail(PKV_ERR_INVALID, "negative num_seqs");
+    if (a->shared_prefix_blocks < 0 || a->shared_prefix_blocks > a->max_blocks)
+        return fail(PKV_ERR_INVALID, "shared_prefix_blocks %d out of 0..max_blocks", a->shared_prefix_blocks);
+    if (a->shared_prefix_blocks > 0 && a->cu_q)
+        return fail(PKV_ERR_UNSUPPORTED, "a shared prefix is a decode-only option");
+    if (a->shared_prefix_blocks > 0 && c->kv_dtype == PKV_F32)
+        return fail(PKV_ERR_UNSUPPORTED, "a shared prefix needs a bf16, fp8 or int8 cache");
     if (a->num_seqs == 0) return PKV_OK;
     if (!a->q || !a->out || !a->block_table || !a->kv_lens) return fail(PKV_ERR_INVALID, "null q/out/table/kv_lens");
     if (a->max_blocks <= 0 || a->max_kv_len <= 0)

@@ -52,6 +52,11 @@
 namespace pkv {
 namespace {
 
+// Floats of one (row, query head) state over a shared prefix: unnormalised
+// output [128], running max (log2 units), normaliser, 2 floats of padding
+// (16-byte aligned states).
+constexpr int kPrefixState = kD + 4;
+
 struct DecodeParams {
     const void* q;                  // [rows][hq][128]
     void* out;                      // [rows][hq][128]
@@ -64,12 +69,21 @@ struct DecodeParams {
     int32_t* plan;                  // [rows + 1]: blocks of rows 0..b-1 (0 blocks for an invalid row)
     float* ws_acc;                  // [hkv][Q][2][group][128] partial unnormalised outputs
     float* ws_ml;                   // [hkv][Q][2][group][2] partial (max, normaliser)
+    const float* ws_prefix;         // shared prefix: [parts][rows][hq][kPrefixState] (acc[128], max, normaliser)
+    int32_t prefix_blocks;          // S: every row's table starts with the same S blocks (0 = none)
+    int32_t prefix_parts;           // key ranges the prefix states were computed over
+    int32_t byte_kv;                // one-byte cache: V values carry v_scale
     int32_t rows, num_blocks, hkv, hq, group, max_blocks, max_kv_len, parts;  // parts = Q
     float scale_log2;               // log2(e) / sqrt(d)
 };
 
 __device__ __forceinline__ bool row_valid(int L, const DecodeParams& p) {
-    return L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS;
+    return L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS && L >= p.prefix_blocks * kBS;
+}
+
+// Blocks of a valid row the decode kernel walks: those past the shared prefix.
+__device__ __forceinline__ int suffix_blocks(int L, const DecodeParams& p) {
+    return (L + kBS - 1) / kBS - p.prefix_blocks;
 }
 
 // First block of wavefront i's range for a head with U blocks over Q parts.
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
         if (b < p.rows) {
             const int L = p.kv_lens[b];
             invalid = !row_valid(L, p);
-            nb = invalid ? 0 : (L + kBS - 1) / kBS;
+            nb = invalid ? 0 : suffix_blocks(L, p);
         }
         // inclusive scan: within the wave, then across the 16 waves
         int v = nb;
@@ -362,6 +376,29 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
         __syncthreads();
         if (invalid) nan_row<QT>(p, b, 0, 1);  // the whole row becomes NaN
     }
+}
+
+// State of (row, head) qrow over the whole shared prefix from the states of
+// its key ranges: M = max m_i, l = sum l_i 2^(m_i - M), acc = sum acc_i
+// 2^(m_i - M), in range order.  This lane's 32 outputs (d = 16 n + 4 g + i)
+// go to acc; l is the lane group g = 0's share (0 for the others); returns M.
+__device__ __forceinline__ float prefix_state(const DecodeParams& p, int64_t qrow, int g, f32x4_t acc[8], float& l) {
+    const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
+    const float* ps = p.ws_prefix + qrow * kPrefixState;
+    float mx = -INFINITY;
+    for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < p.prefix_parts; ++k) {
+        const float* s = ps + k * stride;
+        const float w = __builtin_amdgcn_exp2f(s[kD] - mx);
+        lsum += s[kD + 1] * w;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] += ld<f32x4_t>(s + 16 * n + 4 * g) * w;
+    }
+    l = g == 0 ? lsum : 0.f;
+    return mx;
 }
 
 // Index of the row holding block position x: plan[b] <= x < plan[b+1]
@@ -395,7 +432,7 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
         if (b < p.rows) {
             const int L = p.kv_lens[b];
             invalid = !row_valid(L, p);
-            nb = invalid ? 0 : (L + kBS - 1) / kBS;
+            nb = invalid ? 0 : suffix_blocks(L, p);
         }
         int v = nb;
 #pragma unroll
@@ -467,13 +504,14 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         const int64_t rb1 = plan[b + 1];
         if (rb1 <= u) continue;  // a row with no blocks
         const int L = p.kv_lens[b];
+        // blocks j0 .. j1 - 1 of the row's walk; logical blocks S + j0 .. S + j1 - 1
         const int j0 = static_cast<int>(u - rb0);
         const int j1 = static_cast<int>((u1 < rb1 ? u1 : rb1) - rb0);
-        const int t0 = j0 * kBS;
-        const int t1 = min(L, j1 * kBS);
+        const int t0 = (p.prefix_blocks + j0) * kBS;
+        const int t1 = min(L, (p.prefix_blocks + j1) * kBS);
         const int nblk = j1 - j0;
         const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * p.group + (head_ok ? r : 0);
-        const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks + j0;
+        const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks + p.prefix_blocks + j0;
 
         typename Tile<KV>::Q q;
         Tile<KV>::load_q(q, static_cast<const char*>(p.q) + qrow * kD * kQBytes, head_ok, g);
@@ -494,6 +532,12 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
             return static_cast<int64_t>(ok ? id : 0) * blk_stride;
         };
         Online o;
+        if (p.prefix_blocks > 0 && j0 == 0) {
+            // the row's first piece starts from its state over the shared
+            // prefix, the states of the prefix's key ranges combined (one lane
+            // group carries the normaliser)
+            o.m = prefix_state(p, qrow, g, o.acc, o.l);
+        }
         const int niter = (nblk + NBUF - 1) / NBUF * NBUF;
         Tile<KV> t[NBUF];
 #pragma unroll
@@ -542,18 +586,47 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 // plan's.
 constexpr int kMaxParts = 4096;
 constexpr int kMergeBatch = 8;
+// One workgroup per (row, kv head) with 128 lanes (one per d) for each of up
+// to 8 query heads of the group at once; the row's plan and wavefront range
+// are worked out once for all its heads.
+constexpr int kMergeHeads = 8;
 template <int QT>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p) {
-    const int64_t qrow = blockIdx.x;
-    const int b = static_cast<int>(qrow / p.hq);
-    const int hq = static_cast<int>(qrow % p.hq);
-    const int kvh = hq / p.group;
-    const int hh = hq % p.group;
-    const int d = threadIdx.x;
+__global__ __launch_bounds__(128 * kMergeHeads) void decode_merge_kernel(const DecodeParams p) {
+    const int b = static_cast<int>(blockIdx.x / p.hkv);
+    const int kvh = static_cast<int>(blockIdx.x % p.hkv);
+    const int d = threadIdx.x & (kD - 1);
+    const int h_first = threadIdx.x / kD;
+    const int h_step = blockDim.x / kD;
     const int64_t U = p.plan[p.rows];
     const int64_t rb0 = p.plan[b];
     const int64_t rb1 = p.plan[b + 1];
-    if (rb1 <= rb0 || U <= 0) return;  // invalid row (NaN written with the plan)
+    if (rb1 <= rb0) {
+        // no blocks past a shared prefix: the row's output is its prefix
+        // state, normalised (an invalid row got NaN with the plan)
+        if (p.prefix_blocks > 0 && row_valid(p.kv_lens[b], p)) {
+            const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
+            const float vs = p.byte_kv ? p.v_scale[kvh] : 1.f;
+            for (int hh = h_first; hh < p.group; hh += h_step) {
+                const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * p.group + hh;
+                const float* ps = p.ws_prefix + qrow * kPrefixState;
+                float mx = -INFINITY;
+                for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
+                float num = 0.f, den = 0.f;
+                for (int k = 0; k < p.prefix_parts; ++k) {
+                    const float w = __builtin_amdgcn_exp2f(ps[k * stride + kD] - mx);
+                    num += ps[k * stride + d] * w;
+                    den += ps[k * stride + kD + 1] * w;
+                }
+                const float o = num * (vs / den);
+                if constexpr (QT == PKV_F32)
+                    static_cast<float*>(p.out)[qrow * kD + d] = o;
+                else
+                    static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
+            }
+        }
+        return;
+    }
+    if (U <= 0) return;
     const int Q = effective_parts(U, p.parts);
     // wavefronts whose ranges meet [rb0, rb1)
     int i0 = static_cast<int>(rb0 * Q / U);
@@ -569,54 +642,57 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeParams p)
     // every later one starts inside this row, so the row is its first piece.
     const int side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
     const int grp = p.group;
-    const int64_t base = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp + hh;
     const float* __restrict__ ws_ml = p.ws_ml;
     const float* __restrict__ ws_acc = p.ws_acc;
-    // piece k (clamped to the last piece) -> workspace slot
+    for (int hh = h_first; hh < grp; hh += h_step) {
+        const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * grp + hh;
+        const int64_t base = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp + hh;
+        // piece k (clamped to the last piece) -> workspace slot
 #define PKV_MERGE_SLOT(k) (base + (2 * min((k), n - 1) + ((k) == 0 ? side0 : 0)) * grp)
-    float2 ml[kMergeBatch];
-    float acc[kMergeBatch];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-        const int64_t sl = PKV_MERGE_SLOT(j);
-        ml[j] = ld<float2>(ws_ml + 2 * sl);
-        acc[j] = ws_acc[sl * kD + d];
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, ml[j].x);  // repeats are real pieces
-    for (int k0 = kMergeBatch; k0 < n; k0 += kMergeBatch) {
-        float m[kMergeBatch];
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) m[j] = ws_ml[2 * PKV_MERGE_SLOT(k0 + j)];
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, m[j]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
-        if (k0 > 0) {
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-                const int64_t sl = PKV_MERGE_SLOT(k0 + j);
-                ml[j] = ld<float2>(ws_ml + 2 * sl);
-                acc[j] = ws_acc[sl * kD + d];
-            }
-        }
+        float2 ml[kMergeBatch];
+        float acc[kMergeBatch];
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-            if (k0 + j < n) {
-                const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
-                num += acc[j] * w;
-                den += ml[j].y * w;
+            const int64_t sl = PKV_MERGE_SLOT(j);
+            ml[j] = ld<float2>(ws_ml + 2 * sl);
+            acc[j] = ws_acc[sl * kD + d];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, ml[j].x);  // repeats are real pieces
+        for (int k0 = kMergeBatch; k0 < n; k0 += kMergeBatch) {
+            float m[kMergeBatch];
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) m[j] = ws_ml[2 * PKV_MERGE_SLOT(k0 + j)];
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, m[j]);
+        }
+        float num = 0.f, den = 0.f;
+        for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+            if (k0 > 0) {
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) {
+                    const int64_t sl = PKV_MERGE_SLOT(k0 + j);
+                    ml[j] = ld<float2>(ws_ml + 2 * sl);
+                    acc[j] = ws_acc[sl * kD + d];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                if (k0 + j < n) {
+                    const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
+                    num += acc[j] * w;
+                    den += ml[j].y * w;
+                }
             }
         }
-    }
 #undef PKV_MERGE_SLOT
-    const float o = num / den;
-    if constexpr (QT == PKV_F32) {
-        static_cast<float*>(p.out)[qrow * kD + d] = o;
-    } else {
-        static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
+        const float o = num / den;
+        if constexpr (QT == PKV_F32) {
+            static_cast<float*>(p.out)[qrow * kD + d] = o;
+        } else {
+            static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
+        }
     }
 }
 
@@ -686,7 +762,10 @@ size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_
     const int64_t group = a->num_q_heads / c->num_kv_heads;
     const int64_t plan = (static_cast<int64_t>(rows) + 1 + 3) / 4 * 4;  // int32, 16-byte multiple
     const int64_t slots = static_cast<int64_t>(c->num_kv_heads) * Q * 2 * group;
-    return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4);
+    const int64_t prefix = a->shared_prefix_blocks > 0
+                               ? static_cast<int64_t>(prefix_parts(c, a, rows)) * rows * a->num_q_heads * kPrefixState
+                               : 0;
+    return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4 + prefix * 4);
 }
 
 // Launch decode over `rows` rows whose q/out/table/kv_lens start at the given
@@ -723,6 +802,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.plan = static_cast<int32_t*>(workspace);
     p.ws_acc = reinterpret_cast<float*>(static_cast<int32_t*>(workspace) + plan_ints);
     p.ws_ml = p.ws_acc + slots * kD;
+    p.prefix_blocks = a->shared_prefix_blocks;
+    p.prefix_parts = a->shared_prefix_blocks > 0 ? prefix_parts(c, a, rows) : 0;
+    p.ws_prefix = a->shared_prefix_blocks > 0 ? p.ws_ml + slots * 2 : nullptr;
+    p.byte_kv = is_byte_dtype(c->kv_dtype) ? 1 : 0;
     p.rows = rows;
     p.num_blocks = c->num_blocks;
     p.hkv = c->num_kv_heads;
@@ -742,6 +825,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
             hipLaunchKernelGGL(decode_plan_kernel<PKV_BF16>, dim3(1), dim3(1024), 0, stream, p);
     }
     mark(0);
+    if (p.prefix_blocks > 0) {
+        const int st = launch_prefix_states(c, a, rows, q, table, const_cast<float*>(p.ws_prefix), stream);
+        if (st) return st;
+    }
     const dim3 g1(static_cast<unsigned>(grid));
     const int depth = decode_pipeline_depth();
     if (local)
@@ -749,11 +836,12 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     else
         launch_decode_kernel<false>(c->kv_dtype, depth, g1, stream, p);
     mark(1);
-    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * a->num_q_heads));
+    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads));
+    const dim3 mblock(static_cast<unsigned>(kD * (p.group < kMergeHeads ? p.group : kMergeHeads)));
     if (f32)
-        hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, dim3(128), 0, stream, p);
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, mblock, 0, stream, p);
     else
-        hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, dim3(128), 0, stream, p);
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, mblock, 0, stream, p);
     mark(2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

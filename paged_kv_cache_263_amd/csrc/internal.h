@@ -22,4 +22,11 @@ int32_t decode_parts(const pkv_cache* c, const pkv_attn_args* a);
 // Workspace the decode part of a call needs (bytes; 0 when it has no rows).
 size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_t rows);
 
+// Shared-prefix pass of a decode call (a->shared_prefix_blocks > 0): every
+// row's state over each of prefix_parts() ranges of the prefix into states
+// [parts][rows][hq][128 + 4] (prefill.hip).
+int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows);
+int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, const void* q,
+                         const int32_t* table, float* states, void* stream);
+
 }  // namespace pkv

@@ -67,7 +67,19 @@ struct PrefillParams {
     const int32_t* cu_q;    // [num_seqs + 1]
     int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
+    // shared-prefix pass (PREFIX kernels): the decode rows' queries (one per
+    // row, total_q rows) over the first prefix_tokens keys of table row 0, no
+    // causal mask, the keys split into prefix_parts ranges of whole
+    // iterations; the state of (part, row, head) goes to
+    // states[part][row][hq][kPrefixState]
+    float* states;
+    int32_t prefix_tokens, prefix_parts;
 };
+
+// Floats of one (row, query head) shared-prefix state: unnormalised output
+// [128], running max (log2 units), normaliser, padding (the decode kernel
+// reads the same layout).
+constexpr int kPrefixState = kD + 4;
 
 // LDS element offset of tokens 8 h .. 8 h + 7 of d row d inside a staged V
 // tile: rows of 16 tokens, the two halves swapped in rows with bit 3 of d
@@ -137,7 +149,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int KV>
+// PREFIX: the shared-prefix pass of a decode call (see PrefillParams); else a
+// chunked-prefill row.
+template <int KV, bool PREFIX>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
@@ -150,20 +164,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const int g = lane >> 5;    // lane group
     // blockIdx -> (row, q tile, kv head), kv head fastest (one kv head per XCD).
     const int per_row = p.q_tiles * p.hkv;
-    const int row = p.row0 + blockIdx.x / per_row;
-    const int rem = blockIdx.x % per_row;
-    const int qt = rem / p.hkv;
-    const int kvh = rem % p.hkv;
+    const int row = PREFIX ? 0 : p.row0 + blockIdx.x / per_row;
+    const int kvh = blockIdx.x % p.hkv;
+    const int qt = PREFIX ? blockIdx.x / (p.hkv * p.prefix_parts) : (blockIdx.x % per_row) / p.hkv;
+    const int part = PREFIX ? (blockIdx.x / p.hkv) % p.prefix_parts : 0;
 
-    const int qbeg = p.cu_q[row];
-    const int C = p.cu_q[row + 1] - qbeg;
+    const int qbeg = PREFIX ? 0 : p.cu_q[row];
+    const int C = PREFIX ? p.total_q : p.cu_q[row + 1] - qbeg;
     const int j0 = qt * p.tile_tokens;
     if (j0 >= C || qbeg < 0 || qbeg + C > p.total_q) return;  // (a malformed cu_q writes nothing)
-    const int L = p.kv_lens[row];
-    const bool row_ok = C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS;
-    const int P = L - C;
+    // P: keys before the chunk (prefix pass: the prefix; every query sees all of it)
+    const int L = PREFIX ? p.prefix_tokens : p.kv_lens[row];
+    const bool row_ok = PREFIX ? L >= kBS : C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS;
+    const int P = PREFIX ? L : L - C;
     const int jmax = min(j0 + p.tile_tokens, C);  // exclusive
-    const int kend = row_ok ? P + jmax : 0;       // keys this tile needs
+    const int kend = row_ok ? (PREFIX ? P : P + jmax) : 0;  // keys this tile needs
     const int n_iter = (kend + kKeys - 1) / kKeys;
     const int nblk_seq = (L + kBS - 1) / kBS;
     const int64_t blk_bytes = static_cast<int64_t>(p.hkv) * kTile * kElt;
@@ -176,7 +191,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const int hh = n - tok * p.group;
     const bool qrow_ok = tok < p.tile_tokens && j0 + tok < C;
     const int j = min(j0 + tok, C - 1);
-    const int qpos = P + j;  // keys 0..qpos are visible
+    const int qpos = PREFIX ? P - 1 : P + j;    // keys 0..qpos are visible
+    const int first_pos = PREFIX ? P - 1 : P + j0;  // the smallest qpos in the tile
 
     float scale = p.scale_log2;
     float vscale = 1.f;
@@ -274,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[16 * kt + i] = s[kt][i];
-        if (kbase + kKeys - 1 > P + j0) {
+        if (kbase + kKeys - 1 > first_pos) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -331,22 +347,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // are issued before iteration it is computed and stored to the other LDS
     // buffer after it.  The loads are unconditional (clamped iteration), so no
     // branch sits between a load and its use.
+    // (a prefix-pass workgroup walks its part's range of iterations)
+    const int it_begin = PREFIX ? static_cast<int>(static_cast<int64_t>(n_iter) * part / p.prefix_parts) : 0;
+    const int it_end = PREFIX ? static_cast<int>(static_cast<int64_t>(n_iter) * (part + 1) / p.prefix_parts) : n_iter;
     Stage<KV> sreg;
-    const int last = max(n_iter - 1, 0);
-    stage_load(sreg, 0);
-    if (n_iter > 0) stage_store(sreg, 0, 0);
+    const int last = max(it_end - 1, it_begin);
+    stage_load(sreg, it_begin);
+    if (it_end > it_begin) stage_store(sreg, it_begin, 0);
     __syncthreads();
-    for (int it = 0; it < n_iter; ++it) {
-        const int cur = it & 1;
+    for (int it = it_begin; it < it_end; ++it) {
+        const int cur = (it - it_begin) & 1;
         stage_load(sreg, min(it + 1, last));
         compute(it, cur);
-        if (it + 1 < n_iter) stage_store(sreg, it + 1, cur ^ 1);
+        if (it + 1 < it_end) stage_store(sreg, it + 1, cur ^ 1);
         __syncthreads();
     }
 
     bad = bad || !row_ok;
     l += __shfl_xor(l, 32);
     if (!qrow_ok) return;
+    if constexpr (PREFIX) {  // the state, unnormalised (the decode kernel continues from it)
+        const float nan = __builtin_nanf("");
+        float* sp = p.states + ((static_cast<int64_t>(part) * p.total_q + j) * p.hq + kvh * p.group + hh) * kPrefixState;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4_t v = {acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]};
+                st<f32x4_t>(sp + 32 * dt + 8 * q4 + 4 * g, bad ? f32x4_t{nan, nan, nan, nan} : v);
+            }
+        if (g == 0) st<float2>(sp + kD, float2{m, bad ? nan : l});
+        return;
+    }
     const float inv = bad ? __builtin_nanf("") : vscale / l;
     uint16_t* op = static_cast<uint16_t*>(p.out) +
                    (static_cast<int64_t>(qbeg + j) * p.hq + kvh * p.group + hh) * kD;
@@ -362,6 +394,60 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 }
 
 }  // namespace
+
+// Key ranges the shared-prefix pass splits into: enough workgroups for two
+// per compute unit, each range at least one 64-key iteration, at most 8.
+int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {
+    const int32_t group = a->num_q_heads / c->num_kv_heads;
+    const int64_t tiles = static_cast<int64_t>((rows + kRows / group - 1) / (kRows / group)) * c->num_kv_heads;
+    const int64_t iters = (static_cast<int64_t>(a->shared_prefix_blocks) * kBS + kKeys - 1) / kKeys;
+    int64_t parts = (512 + tiles - 1) / tiles;
+    parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+    return static_cast<int>(parts < iters ? parts : (iters < 1 ? 1 : iters));
+}
+
+// The shared-prefix pass of a decode call: every row's (query head) state over
+// the first 16 * S tokens of table row 0, into states [rows][hq][kPrefixState].
+int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, const void* q,
+                         const int32_t* table, float* states, void* stream_ptr) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (c->kv_dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "a shared prefix needs a bf16, fp8 or int8 cache");
+    const int32_t group = a->num_q_heads / c->num_kv_heads;
+    const int32_t tile_tokens = kRows / group;
+    const int32_t q_tiles = (rows + tile_tokens - 1) / tile_tokens;
+    const int64_t elt = c->kv_dtype == PKV_BF16 ? 2 : 1;
+    const int64_t layer_elems = static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * kTile;
+    PrefillParams p{};
+    p.q = q;
+    p.k_pool = static_cast<const char*>(c->k_pool) + a->layer * layer_elems * elt;
+    p.v_pool = static_cast<const char*>(c->v_pool) + a->layer * layer_elems * elt;
+    p.k_scale = c->k_scale ? c->k_scale + static_cast<int64_t>(a->layer) * c->num_kv_heads : nullptr;
+    p.v_scale = c->v_scale ? c->v_scale + static_cast<int64_t>(a->layer) * c->num_kv_heads : nullptr;
+    p.table = table;
+    p.row0 = 0;
+    p.num_blocks = c->num_blocks;
+    p.hkv = c->num_kv_heads;
+    p.hq = a->num_q_heads;
+    p.group = group;
+    p.max_blocks = a->max_blocks;
+    p.max_kv_len = a->max_kv_len;
+    p.q_tiles = q_tiles;
+    p.total_q = rows;
+    p.tile_tokens = tile_tokens;
+    p.scale_log2 = kLog2e / sqrtf(static_cast<float>(kD));
+    p.states = states;
+    p.prefix_tokens = a->shared_prefix_blocks * kBS;
+    p.prefix_parts = prefix_parts(c, a, rows);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(q_tiles) * c->num_kv_heads * p.prefix_parts));
+    if (c->kv_dtype == PKV_BF16)
+        hipLaunchKernelGGL((prefill_kernel<PKV_BF16, true>), grid, dim3(256), 0, stream, p);
+    else if (c->kv_dtype == PKV_FP8_E4M3)
+        hipLaunchKernelGGL((prefill_kernel<PKV_FP8_E4M3, true>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<PKV_INT8, true>), grid, dim3(256), 0, stream, p);
+    return PKV_OK;
+}
+
 }  // namespace pkv
 
 using pkv::fail;
@@ -418,11 +504,11 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.tile_tokens = tile_tokens;
     p.scale_log2 = pkv::kLog2e / sqrtf(static_cast<float>(pkv::kD));
     if (c->kv_dtype == PKV_BF16)
-        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_BF16>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_BF16, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     else if (c->kv_dtype == PKV_FP8_E4M3)
-        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_FP8_E4M3>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_FP8_E4M3, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL(pkv::prefill_kernel<PKV_INT8>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_INT8, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
     if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

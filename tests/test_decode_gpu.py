@@ -316,3 +316,50 @@ def test_unwritten_slots_hold_nan(kv):
     blocks hold NaN bit patterns: masked tokens must not reach the output."""
     w = W.custom([1, 17, 300, 513, 1000], 8, 2, kv, seed=91, variant="peaked")
     check_decode(w, hip=HipSide(w, fill_byte=0xFF))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("variant", ["peaked", "needle"])
+def test_shared_prefix_pass(kv, variant):
+    """Decode with the shared-prefix promise (attention over the 125 common
+    blocks computed once for all rows, each row continued from that state)
+    matches the oracle, agrees with the plain decode within tolerance, and is
+    deterministic."""
+    w = W.shared_prefix(nseq=64, max_suffix=400, hq=64, hkv=8, variant=variant)
+    if kv == "int8":
+        w = W.scaled_int8(w)
+    hip = HipSide(w)
+    rows = [0, 1, 2, 31, 62, 63]
+    _, out = check_decode(w, rows=rows, hip=hip, shared_prefix_blocks=125)
+    plain = hip.decode()
+    again = hip.decode(shared_prefix_blocks=125)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    assert (out.float() - plain.float()).abs().max().item() <= 2 * TOL[w.kv_dtype]
+
+
+def test_shared_prefix_pass_rows_without_suffix():
+    """Rows that end exactly at the shared prefix take their output from the
+    prefix state alone; a row shorter than the prefix is invalid (NaN)."""
+    import paged_kv_cache_263_amd as pk
+
+    w = W.shared_prefix(nseq=8, prefix=64, hq=16, hkv=2, variant="peaked",
+                        suffixes=[0, 0, 5, 16, 0, 33, 7, 9])
+    hip = HipSide(w)
+    case("shared prefix: rows without suffix")
+    assert [hip.lens[b] for b in range(8)][:2] == [64, 64]
+    check_decode(w, hip=hip, shared_prefix_blocks=4)
+    lens = hip.kv_lens.clone()
+    lens[3] = 40  # shorter than the 64-token prefix
+    out = pk.paged_attn_decode(hip.cache, hip.q, hip.table, lens, hip.max_kv_len, shared_prefix_blocks=4)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[3].float()).all() and torch.isfinite(out[2].float()).all()
+
+
+def test_shared_prefix_pass_placement_invariance():
+    w = W.shared_prefix(nseq=32, max_suffix=300, hq=32, hkv=8, variant="needle")
+    case("shared prefix: placement invariance")
+    a = HipSide(w).decode(shared_prefix_blocks=125)
+    b = HipSide(w, placement=np.arange(w.num_blocks, dtype=np.int32)).decode(shared_prefix_blocks=125)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -81,6 +81,8 @@ class Workload:
     # positions of the tokens each sequence wrote itself: seq -> list of (start, stop)
     own_ranges: dict = field(default_factory=dict)
     num_layers: int = 1
+    # shared_prefix only: tokens of the prefix every sequence shares
+    shared_prefix_tokens: int = 0
 
     @property
     def group(self) -> int:
@@ -150,13 +152,17 @@ def llama8b(seed: int = 2, variant: str = "plain", batch: int = 64,
 
 def shared_prefix(seed: int = 3, variant: str = "plain", nseq: int = 256,
                   prefix: int = 2000, min_suffix: int = 50, max_suffix: int = 1000,
-                  hq: int = 64, hkv: int = 8) -> Workload:
+                  hq: int = 64, hkv: int = 8, suffixes=None) -> Workload:
     """Sequence 0 writes the prefix; sequences 1..nseq-2 share its blocks and add
     their own suffix.  The last sequence forks sequence nseq-2 when that one
     holds prefix + r tokens (r not a multiple of 16), then both append the rest
-    of their own suffixes: the first of them to write triggers the one copy."""
+    of their own suffixes: the first of them to write triggers the one copy.
+    ``suffixes`` (one per sequence; the last two at least 2) replaces the drawn
+    suffix lengths."""
     rng = np.random.default_rng(seed)
     suffix = [int(x) for x in rng.integers(min_suffix, max_suffix + 1, size=nseq)]
+    if suffixes is not None:
+        suffix = [int(x) for x in suffixes]
     script, own = [], {}
     op = 0
     script.append(Op("create"))
@@ -184,7 +190,7 @@ def shared_prefix(seed: int = 3, variant: str = "plain", nseq: int = 256,
     logical = sum(_blocks(prefix + suffix[s]) for s in range(nseq - 1)) + _blocks(prefix + r + suffix[c])
     nb = _pool_size(logical)
     return Workload("shared_prefix", hq, hkv, 128, "bf16", "bf16", nb, placement(nb, seed), script,
-                    list(range(nseq)), [1] * nseq, seed, variant, own_ranges=own)
+                    list(range(nseq)), [1] * nseq, seed, variant, own_ranges=own, shared_prefix_tokens=prefix)
 
 
 def chunked(context: int = 16384, chunk: int = 1024, n_decode: int = 32, decode_len: int = 4096,
