@@ -579,24 +579,33 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
 // Merge the pieces of one (row, query head) that was divided between
 // wavefronts: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
-// M = max_i m_i, in wavefront order.  One lane per d.  The pieces are read
-// kMergeBatch at a time with every load of a batch issued together (indices
-// past the last piece repeat it and are left out of the sums), so a row cut
-// into at most kMergeBatch pieces costs one round of global loads after the
-// plan's.
+// M = max_i m_i, in wavefront order.  The pieces are read kMergeBatch at a
+// time (indices past the last piece repeat it and are left out of the sums).
 constexpr int kMaxParts = 4096;
 constexpr int kMergeBatch = 8;
-// One workgroup per (row, kv head) with 128 lanes (one per d) for each of up
-// to 8 query heads of the group at once; the row's plan and wavefront range
-// are worked out once for all its heads.
-constexpr int kMergeHeads = 8;
+// One wavefront per (row, kv head); lane l owns d = 2 l, 2 l + 1 of every
+// query head of the group.  The row's plan and wavefront range are worked out
+// once; then, for kMergeHeads heads at a time, the pieces are read with every
+// load of a batch issued together, so a row cut into at most kMergeBatch
+// pieces costs one round of loads per kMergeHeads heads after the plan's.
+constexpr int kMergeHeads = 4;
+
 template <int QT>
-__global__ __launch_bounds__(128 * kMergeHeads) void decode_merge_kernel(const DecodeParams p) {
+__device__ __forceinline__ void store_out2(void* out, int64_t qrow, int d, float a, float b) {
+    if constexpr (QT == PKV_F32) {
+        st<float2>(static_cast<float*>(out) + qrow * kD + d, float2{a, b});
+    } else {
+        st<uint32_t>(static_cast<uint16_t*>(out) + qrow * kD + d, bf16_bits_rne(a) | (bf16_bits_rne(b) << 16));
+    }
+}
+
+template <int QT>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) {
     const int b = static_cast<int>(blockIdx.x / p.hkv);
     const int kvh = static_cast<int>(blockIdx.x % p.hkv);
-    const int d = threadIdx.x & (kD - 1);
-    const int h_first = threadIdx.x / kD;
-    const int h_step = blockDim.x / kD;
+    const int d = 2 * threadIdx.x;
+    const int grp = p.group;
+    const int64_t row_q = static_cast<int64_t>(b) * p.hq + kvh * grp;  // query row of head 0 of the group
     const int64_t U = p.plan[p.rows];
     const int64_t rb0 = p.plan[b];
     const int64_t rb1 = p.plan[b + 1];
@@ -606,22 +615,21 @@ __global__ __launch_bounds__(128 * kMergeHeads) void decode_merge_kernel(const D
         if (p.prefix_blocks > 0 && row_valid(p.kv_lens[b], p)) {
             const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
             const float vs = p.byte_kv ? p.v_scale[kvh] : 1.f;
-            for (int hh = h_first; hh < p.group; hh += h_step) {
-                const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * p.group + hh;
-                const float* ps = p.ws_prefix + qrow * kPrefixState;
+            for (int hh = 0; hh < grp; ++hh) {
+                const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
                 float mx = -INFINITY;
                 for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
-                float num = 0.f, den = 0.f;
+                float2 num = {0.f, 0.f};
+                float den = 0.f;
                 for (int k = 0; k < p.prefix_parts; ++k) {
                     const float w = __builtin_amdgcn_exp2f(ps[k * stride + kD] - mx);
-                    num += ps[k * stride + d] * w;
+                    const float2 a = ld<float2>(ps + k * stride + d);
+                    num.x += a.x * w;
+                    num.y += a.y * w;
                     den += ps[k * stride + kD + 1] * w;
                 }
-                const float o = num * (vs / den);
-                if constexpr (QT == PKV_F32)
-                    static_cast<float*>(p.out)[qrow * kD + d] = o;
-                else
-                    static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
+                const float inv = vs / den;
+                store_out2<QT>(p.out, row_q + hh, d, num.x * inv, num.y * inv);
             }
         }
         return;
@@ -641,59 +649,72 @@ __global__ __launch_bounds__(128 * kMergeHeads) void decode_merge_kernel(const D
     // its range in an earlier row (then this row is its second piece, side 1);
     // every later one starts inside this row, so the row is its first piece.
     const int side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
-    const int grp = p.group;
     const float* __restrict__ ws_ml = p.ws_ml;
     const float* __restrict__ ws_acc = p.ws_acc;
-    for (int hh = h_first; hh < grp; hh += h_step) {
-        const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * grp + hh;
-        const int64_t base = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp + hh;
-        // piece k (clamped to the last piece) -> workspace slot
-#define PKV_MERGE_SLOT(k) (base + (2 * min((k), n - 1) + ((k) == 0 ? side0 : 0)) * grp)
-        float2 ml[kMergeBatch];
-        float acc[kMergeBatch];
+    const int64_t base0 = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp;
+    // slot of (head hh, piece k), the piece clamped to the last one
+#define PKV_MERGE_SLOT(hh, k) (base0 + (hh) + (2 * min((k), n - 1) + ((k) == 0 ? side0 : 0)) * grp)
+    for (int h0 = 0; h0 < grp; h0 += kMergeHeads) {
+        float mx[kMergeHeads];
+        float2 num[kMergeHeads];
+        float den[kMergeHeads];
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-            const int64_t sl = PKV_MERGE_SLOT(j);
-            ml[j] = ld<float2>(ws_ml + 2 * sl);
-            acc[j] = ws_acc[sl * kD + d];
+        for (int a = 0; a < kMergeHeads; ++a) {
+            mx[a] = -INFINITY;
+            num[a] = float2{0.f, 0.f};
+            den[a] = 0.f;
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, ml[j].x);  // repeats are real pieces
-        for (int k0 = kMergeBatch; k0 < n; k0 += kMergeBatch) {
-            float m[kMergeBatch];
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) m[j] = ws_ml[2 * PKV_MERGE_SLOT(k0 + j)];
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) mx = fmaxf(mx, m[j]);
-        }
-        float num = 0.f, den = 0.f;
+        // first pass: the running max (one batch of loads when n <= kMergeBatch)
+        float2 ml[kMergeHeads][kMergeBatch];
+        float2 acc[kMergeHeads][kMergeBatch];
         for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
-            if (k0 > 0) {
+#pragma unroll
+            for (int a = 0; a < kMergeHeads; ++a) {
+                const int hh = min(h0 + a, grp - 1);
 #pragma unroll
                 for (int j = 0; j < kMergeBatch; ++j) {
-                    const int64_t sl = PKV_MERGE_SLOT(k0 + j);
-                    ml[j] = ld<float2>(ws_ml + 2 * sl);
-                    acc[j] = ws_acc[sl * kD + d];
+                    const int64_t sl = PKV_MERGE_SLOT(hh, k0 + j);
+                    ml[a][j] = ld<float2>(ws_ml + 2 * sl);
+                    acc[a][j] = ld<float2>(ws_acc + sl * kD + d);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-                if (k0 + j < n) {
-                    const float w = __builtin_amdgcn_exp2f(ml[j].x - mx);
-                    num += acc[j] * w;
-                    den += ml[j].y * w;
+            for (int a = 0; a < kMergeHeads; ++a)
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) mx[a] = fmaxf(mx[a], ml[a][j].x);  // repeats are real pieces
+        }
+        // second pass: the weighted sums, in piece order (the loads of a row
+        // cut into at most kMergeBatch pieces are still in registers)
+        for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+            if (n > kMergeBatch) {
+#pragma unroll
+                for (int a = 0; a < kMergeHeads; ++a) {
+                    const int hh = min(h0 + a, grp - 1);
+#pragma unroll
+                    for (int j = 0; j < kMergeBatch; ++j) {
+                        const int64_t sl = PKV_MERGE_SLOT(hh, k0 + j);
+                        ml[a][j] = ld<float2>(ws_ml + 2 * sl);
+                        acc[a][j] = ld<float2>(ws_acc + sl * kD + d);
+                    }
                 }
             }
+#pragma unroll
+            for (int a = 0; a < kMergeHeads; ++a)
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) {
+                    if (k0 + j < n) {
+                        const float w = __builtin_amdgcn_exp2f(ml[a][j].x - mx[a]);
+                        num[a].x += acc[a][j].x * w;
+                        num[a].y += acc[a][j].y * w;
+                        den[a] += ml[a][j].y * w;
+                    }
+                }
         }
-#undef PKV_MERGE_SLOT
-        const float o = num / den;
-        if constexpr (QT == PKV_F32) {
-            static_cast<float*>(p.out)[qrow * kD + d] = o;
-        } else {
-            static_cast<uint16_t*>(p.out)[qrow * kD + d] = static_cast<uint16_t>(bf16_bits_rne(o));
-        }
+#pragma unroll
+        for (int a = 0; a < kMergeHeads; ++a)
+            if (h0 + a < grp) store_out2<QT>(p.out, row_q + h0 + a, d, num[a].x / den[a], num[a].y / den[a]);
     }
+#undef PKV_MERGE_SLOT
 }
 
 // Blocks in flight per wavefront (2..4).  PKV_DECODE_DEPTH overrides the
@@ -837,11 +858,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
         launch_decode_kernel<false>(c->kv_dtype, depth, g1, stream, p);
     mark(1);
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads));
-    const dim3 mblock(static_cast<unsigned>(kD * (p.group < kMergeHeads ? p.group : kMergeHeads)));
     if (f32)
-        hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, mblock, 0, stream, p);
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, dim3(64), 0, stream, p);
     else
-        hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, mblock, 0, stream, p);
+        hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, dim3(64), 0, stream, p);
     mark(2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
