@@ -107,6 +107,12 @@ def parse():
                     help="physical block order: the workload's seeded shuffle, or identity (a contiguous control)")
     ap.add_argument("--no-prefix-pass", action="store_true",
                     help="shared_prefix: do not pass the shared-prefix promise (every row reads the prefix itself)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="decode workloads: extra steps after the timed ones, each after writing a 512 MiB scratch "
+                         "buffer (more than the 256 MB last-level cache), timed with events only (reported apart)")
+    ap.add_argument("--cold-flush", choices=["write", "read"], default="read",
+                    help="how the cold-cache steps displace the cache: write the scratch buffer, or read it "
+                         "(written once beforehand, so no dirty lines are left to write back)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows in the oracle sample (0 = auto)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -573,33 +579,36 @@ def main():
     seqs = list(w.batch)
     lens = np.array([pk.seq_len(pool, s) for s in seqs], dtype=np.int64)
     total = args.warmup + args.steps
-    max_blocks = int(math.ceil((lens.max() + total) / 16)) + 1
+    n_steps = total + max(0, args.cold_steps)
+    max_blocks = int(math.ceil((lens.max() + n_steps) / 16)) + 1
     table_h, lens_h = pk.block_table_build(pool, seqs, max_blocks)
     d_table = table_h.to(device)
     d_lens = lens_h.to(device)
     q = __import__("workloads").queries(w, device)
     out = torch.empty_like(q)
     g = torch.Generator(device=device).manual_seed(w.seed + 5)
-    k_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
-    v_new = torch.randn((total, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
+    k_new = torch.randn((n_steps, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
+    v_new = torch.randn((n_steps, B, w.hkv, w.d), generator=g, device=device).to(cache.value_dtype)
     d_rows = torch.arange(B, dtype=torch.int32, device=device)
     # slots and positions of every step, in pinned host memory that the cache
     # write kernel reads directly (one row per step, so no step overwrites
     # values an earlier, still queued step has yet to read)
-    h_io = torch.empty((total, 2, B), dtype=torch.int32).pin_memory()
+    h_io = torch.empty((n_steps, 2, B), dtype=torch.int32).pin_memory()
     ones = [1] * B
     # workspace sized for the longest row the run reaches
     # shared_prefix: every table starts with the prefix's blocks (125 for 2000 tokens)
     spb = w.shared_prefix_tokens // 16 if (w.name == "shared_prefix" and not args.no_prefix_pass) else 0
-    a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + total, 0, args.decode_parts, None)
+    a = pk._args(cache, q, out, d_table, d_lens, int(lens.max()) + n_steps, 0, args.decode_parts, None)
     a.shared_prefix_blocks = spb
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream()
-    ev = TimingEvents(total, 4)
+    ev = TimingEvents(n_steps, 4)
     torch.cuda.synchronize()
 
     kv_bytes_step = []
+    unique_bytes_step = []  # distinct KV bytes: a prefix every row shares counts once
     copies_total = 0
+    shared_tokens = w.shared_prefix_tokens if w.name == "shared_prefix" else 0
 
     def step(i):
         nonlocal copies_total
@@ -620,6 +629,7 @@ def main():
                              workspace=ws, events=ev.handles(i, (1, 2, 3) if breakdown else (1, 2)),
                              shared_prefix_blocks=spb)
         kv_bytes_step.append(int(lens.sum()) * w.hkv * w.d * 2 * elt_bytes(w))
+        unique_bytes_step.append((int(lens.sum()) - (B - 1) * shared_tokens) * w.hkv * w.d * 2 * elt_bytes(w))
 
     for i in range(args.warmup):
         step(i)
@@ -632,6 +642,21 @@ def main():
         host += time.perf_counter() - h0
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    # cold-cache steps (after the timed ones; not part of value): the last-level
+    # cache holds a scratch buffer, not KV, when each step starts
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=device) if args.cold_steps > 0 else None
+    if scratch is not None and args.cold_flush == "read":
+        scratch.fill_(1)
+        scratch.view(torch.int32).sum()
+    for i in range(total, n_steps):
+        if args.cold_flush == "write":
+            scratch.fill_(i & 0xFF)
+        else:
+            scratch.view(torch.int32).sum()
+        step(i)
+    torch.cuda.synchronize()
+    cold_ms = [ev.ms(i, 1, 2) for i in range(total, n_steps)]
+    del scratch
 
     timed = range(args.warmup, total)
     split_ms = [ev.ms(i, 1, 2) for i in timed]  # decode kernel
@@ -642,12 +667,13 @@ def main():
     def us(v):
         return round(float(np.mean(v)) * 1e3, 2) if v else None
 
-    bytes_timed = kv_bytes_step[args.warmup:]
+    bytes_timed = kv_bytes_step[args.warmup:total]
+    unique_timed = unique_bytes_step[args.warmup:total]
     ms_per_step = dt * 1e3 / args.steps
     value = sum(bytes_timed) / dt / 1e9
     tokens_per_s = sum(b / (w.hkv * w.d * 2 * elt_bytes(w)) for b in bytes_timed) / dt
     split_avg_s = float(np.mean(split_ms)) / 1e3
-    achieved = float(np.mean(bytes_timed)) / split_avg_s / 1e9
+    achieved = float(np.mean(unique_timed)) / split_avg_s / 1e9
 
     result = {
         "metric": "paged GQA decode: achieved HBM GB/s (KV bytes) + seq-tokens attended/s, 1 GPU",
@@ -669,11 +695,15 @@ def main():
         "seq_tokens_per_s": round(tokens_per_s, 1),
         "kernels_us": {"decode": us(split_ms), "decode_merge_warmup": us(merge_ms),
                        "cache_write_warmup": us(write_ms)},
+        "decode_us_p10_p50_p90": [round(float(np.percentile(split_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "decode_us_cold": us(cold_ms),
+        "cold_flush": args.cold_flush if cold_ms else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if w.name == "llama8b" and not args.decode_parts else None,
-                     "algorithmic_bytes_per_launch": float(np.mean(bytes_timed)),
-                     "kernel": "decode_kernel (KV bytes of all rows per launch / event-timed duration; traffic = "
+                     "algorithmic_bytes_per_launch": float(np.mean(unique_timed)),
+                     "kernel": "decode_kernel (distinct KV bytes of all rows per launch, a prefix all rows share counted once, / "
+                               "event-timed duration of the decode kernel and any shared-prefix pass; traffic = "
                                "HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary)"},
         "copy_on_write_copies": copies_total,
         "host_us_per_step": round(host * 1e6 / args.steps, 1),
