@@ -77,6 +77,13 @@ struct DecodeParams {
     float scale_log2;               // log2(e) / sqrt(d)
 };
 
+// A buffer no wave of the kernel writes, read through the constant address
+// space, so that wave-uniform reads of it become scalar loads.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* readonly_scalar(const T* ptr) {
+    return (const __attribute__((address_space(4))) T*)(ptr);
+}
+
 __device__ __forceinline__ bool row_valid(int L, const DecodeParams& p) {
     return L >= 1 && L <= p.max_kv_len && L <= p.max_blocks * kBS && L >= p.prefix_blocks * kBS;
 }
@@ -382,20 +389,44 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
 // its key ranges: M = max m_i, l = sum l_i 2^(m_i - M), acc = sum acc_i
 // 2^(m_i - M), in range order.  This lane's 32 outputs (d = 16 n + 4 g + i)
 // go to acc; l is the lane group g = 0's share (0 for the others); returns M.
+// The loads are batched (all maxima at once, then two ranges at a time) so a
+// row's first piece waits for a few memory round trips, not two per range.
+constexpr int kMaxPrefixParts = 8;
+
 __device__ __forceinline__ float prefix_state(const DecodeParams& p, int64_t qrow, int g, f32x4_t acc[8], float& l) {
     const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
     const float* ps = p.ws_prefix + qrow * kPrefixState;
+    const int parts = p.prefix_parts;
+    float mk[kMaxPrefixParts];
+#pragma unroll
+    for (int k = 0; k < kMaxPrefixParts; ++k) mk[k] = k < parts ? ps[k * stride + kD] : -INFINITY;
     float mx = -INFINITY;
-    for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
+#pragma unroll
+    for (int k = 0; k < kMaxPrefixParts; ++k) mx = fmaxf(mx, mk[k]);
     float lsum = 0.f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.prefix_parts; ++k) {
-        const float* s = ps + k * stride;
-        const float w = __builtin_amdgcn_exp2f(s[kD] - mx);
-        lsum += s[kD + 1] * w;
+    for (int k = 0; k < parts; k += 2) {
+        const bool two = k + 1 < parts;
+        const float* s0 = ps + k * stride;
+        const float* s1 = two ? s0 + stride : s0;
+        f32x4_t a0[8], a1[8];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] += ld<f32x4_t>(s + 16 * n + 4 * g) * w;
+        for (int n = 0; n < 8; ++n) a0[n] = ld<f32x4_t>(s0 + 16 * n + 4 * g);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) a1[n] = ld<f32x4_t>(s1 + 16 * n + 4 * g);
+        const float2 ml0 = ld<float2>(s0 + kD);
+        const float2 ml1 = ld<float2>(s1 + kD);
+        const float w0 = __builtin_amdgcn_exp2f(ml0.x - mx);
+        lsum += ml0.y * w0;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] += a0[n] * w0;
+        if (two) {
+            const float w1 = __builtin_amdgcn_exp2f(ml1.x - mx);
+            lsum += ml1.y * w1;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[n] += a1[n] * w1;
+        }
     }
     l = g == 0 ? lsum : 0.f;
     return mx;
@@ -423,6 +454,21 @@ constexpr int kLocalPlanRows = 1024;
 
 template <int QT>
 __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_sh, int lane) {
+    // Every row length is requested before the first is used (one memory
+    // round trip, not one per 64 rows) and parked in this lane's own plan
+    // slots, which the scan below overwrites in the same order.
+    constexpr int kPer = kLocalPlanRows / 64;
+    int lens[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int b = 64 * k + lane;
+        lens[k] = b < p.rows ? p.kv_lens[b] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int b = 64 * k + lane;
+        if (b < p.rows) plan_sh[b + 1] = lens[k];
+    }
     int carry = 0;
 #pragma unroll 1
     for (int base = 0; base < p.rows; base += 64) {
@@ -430,7 +476,7 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
         int nb = 0;
         bool invalid = false;
         if (b < p.rows) {
-            const int L = p.kv_lens[b];
+            const int L = plan_sh[b + 1];
             invalid = !row_valid(L, p);
             nb = invalid ? 0 : suffix_blocks(L, p);
         }
@@ -461,12 +507,14 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
     __syncthreads();
 }
 
-template <int KV, int NBUF, bool LOCAL_PLAN>
+template <int KV, bool LOCAL_PLAN>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
     using Elt = typename Tile<KV>::Elt;
+    using QReg = typename Tile<KV>::Q;
+    constexpr int kQRegs = static_cast<int>(sizeof(QReg) / sizeof(QReg{}[0]));
     const int lane = threadIdx.x;
     const int r = lane & 15;
     const int g = lane >> 4;
@@ -476,8 +524,19 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     const int kvh = blockIdx.x % p.hkv;
     const int wi = blockIdx.x / p.hkv;
     if constexpr (LOCAL_PLAN) local_plan<QT>(p, plan_sh, lane);
-    const int32_t* plan = LOCAL_PLAN ? plan_sh : p.plan;
-    const int64_t U = plan[p.rows];
+    // The plan, the row lengths and the block table are read wave-uniformly:
+    // the plan from LDS (or, when the plan kernel wrote it, through the
+    // constant address space) and the other two through the constant address
+    // space, so these reads are LDS reads or scalar loads.  A vector load
+    // there would be counted with the tile loads, and waiting for it would
+    // wait for every tile still in flight.
+    const auto* cplan = readonly_scalar(p.plan);
+    auto plan_at = [&](int i) -> int64_t {
+        return __builtin_amdgcn_readfirstlane(LOCAL_PLAN ? plan_sh[i] : cplan[i]);
+    };
+    const auto* ctable = readonly_scalar(p.table);
+    const auto* clens = readonly_scalar(p.kv_lens);
+    const int64_t U = plan_at(p.rows);
     const int Q = effective_parts(U, p.parts);
     if (wi >= Q || U <= 0) return;
     const int64_t u0 = range_start(U, wi, Q);
@@ -496,84 +555,117 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     const Elt* kpool = static_cast<const Elt*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile;
     const Elt* vpool = static_cast<const Elt*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile;
     const int64_t blk_stride = static_cast<int64_t>(p.hkv) * kTile;
+    auto qrow_of = [&](int row) {
+        return static_cast<int64_t>(row) * p.hq + kvh * p.group + (head_ok ? r : 0);
+    };
+    auto q_ptr = [&](int row) { return static_cast<const char*>(p.q) + qrow_of(row) * kD * kQBytes; };
 
-    int b = find_row(plan, p.rows, u0);
-    const int b_first = b;
-    for (int64_t u = u0; u < u1; ++b) {
-        const int64_t rb0 = plan[b];
-        const int64_t rb1 = plan[b + 1];
-        if (rb1 <= u) continue;  // a row with no blocks
-        const int L = p.kv_lens[b];
-        // blocks j0 .. j1 - 1 of the row's walk; logical blocks S + j0 .. S + j1 - 1
-        const int j0 = static_cast<int>(u - rb0);
-        const int j1 = static_cast<int>((u1 < rb1 ? u1 : rb1) - rb0);
-        const int t0 = (p.prefix_blocks + j0) * kBS;
-        const int t1 = min(L, (p.prefix_blocks + j1) * kBS);
-        const int nblk = j1 - j0;
-        const int64_t qrow = static_cast<int64_t>(b) * p.hq + kvh * p.group + (head_ok ? r : 0);
-        const int32_t* trow = p.table + static_cast<int64_t>(b) * p.max_blocks + p.prefix_blocks + j0;
-
-        typename Tile<KV>::Q q;
-        Tile<KV>::load_q(q, static_cast<const char*>(p.q) + qrow * kD * kQBytes, head_ok, g);
-
-        // Ring of NBUF register tiles: while block j is computed, blocks
-        // j+1 .. j+NBUF-1 are in flight.  The trip count is padded to a
-        // multiple of NBUF and every load is unconditional (block index
-        // clamped to the piece's last block, a cache hit), so no branch sits
-        // between a load and its use and the wait counts keep the prefetched
-        // loads in flight.  Padding steps are fully masked and change nothing.
-        // A block id outside the pool is replaced by block 0 and marks the
-        // piece bad (its output becomes NaN).
-        bool bad = false;
-        auto tile_off = [&](int j) -> int64_t {
-            int32_t id = trow[min(j, nblk - 1)];
-            const bool ok = id >= 0 && id < p.num_blocks;
-            bad = bad || !ok;
-            return static_cast<int64_t>(ok ? id : 0) * blk_stride;
-        };
-        Online o;
-        if (p.prefix_blocks > 0 && j0 == 0) {
-            // the row's first piece starts from its state over the shared
-            // prefix, the states of the prefix's key ranges combined (one lane
-            // group carries the normaliser)
-            o.m = prefix_state(p, qrow, g, o.acc, o.l);
+    // The wavefront's blocks u0 .. u1 - 1 (rows in order, each row's blocks
+    // in order) stream through a ring of two register tiles: while block x is
+    // computed, block x + 1 is in flight, also across the end of a row, so a
+    // new row does not start with a wait for its first tile.  Two cursors
+    // walk the rows: the load cursor (row bl, blocks lrb0 .. lrb1 - 1) one
+    // block ahead of the compute cursor (row bc).  Entering a row, the load
+    // cursor also requests that row's query, which the compute cursor takes
+    // over when it gets there.  A block id outside the pool is replaced by
+    // block 0 and marks its tile bad (the piece's output becomes NaN).
+    const int b_first = __builtin_amdgcn_readfirstlane(find_row(LOCAL_PLAN ? plan_sh : p.plan, p.rows, u0));
+    int bl = b_first;
+    int64_t lrb0 = plan_at(bl), lrb1 = plan_at(bl + 1);
+    int l_len = clens[bl];  // kv_len of row bl
+    QReg q, q_next;
+    auto issue = [&](Tile<KV>& t, bool& tbad, int64_t x) {
+        if (lrb1 <= x) {
+            do {
+                ++bl;
+                lrb0 = lrb1;
+                lrb1 = plan_at(bl + 1);
+            } while (lrb1 <= x);
+            l_len = clens[bl];
+            Tile<KV>::load_q(q_next, q_ptr(bl), head_ok, g);
         }
-        const int niter = (nblk + NBUF - 1) / NBUF * NBUF;
-        Tile<KV> t[NBUF];
+        const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + p.prefix_blocks + (x - lrb0)];
+        const bool ok = id >= 0 && id < p.num_blocks;
+        tbad = !ok;
+        const int64_t off = static_cast<int64_t>(ok ? id : 0) * blk_stride;
+        t.load(kpool + off, vpool + off, r, g);
+    };
+
+    Tile<KV> t[2];
+    bool tbad[2];
+    issue(t[0], tbad[0], u0);
+    Tile<KV>::load_q(q, q_ptr(b_first), head_ok, g);
+
+    // compute cursor: row bc with blocks crb0 .. crb1 - 1; the piece (this
+    // wavefront's part of the row) ends at flat block piece_end; tokens at or
+    // past t1 are masked
+    int bc = b_first;
+    int64_t crb0 = lrb0, crb1 = lrb1;
+    int c_len = l_len;
+    int64_t piece_end = u0;  // forces the set-up of the first piece
+    int t1 = 0;
+    bool pbad = false;
+    Online o;
+    // One block x: computed from `cur` while block x + 1 (the range's last
+    // block again at its end: a cache hit, never used) loads into `nxt`.  A
+    // new row's query is taken over from q_next before that load, which may
+    // request the query of the row after.
+    auto step = [&](Tile<KV>& cur, bool tb, Tile<KV>& nxt, bool& nb, int64_t x) {
+        const bool first = x == piece_end;  // first block of a piece
+        if (first && x > u0) {
+            // a later row: the load cursor, which loaded block x, is still in
+            // it, with its bounds, length and query
+            bc = bl;
+            crb0 = lrb0;
+            crb1 = lrb1;
+            c_len = l_len;
 #pragma unroll
-        for (int v = 0; v < NBUF - 1; ++v) {
-            const int64_t off = tile_off(v);
-            t[v].load(kpool + off, vpool + off, r, g);
+            for (int i = 0; i < kQRegs; ++i) q[i] = q_next[i];
         }
-        for (int jb = 0; jb < niter; jb += NBUF) {
-#pragma unroll
-            for (int v = 0; v < NBUF; ++v) {
-                const int j = jb + v;
-                const int64_t off = tile_off(j + NBUF - 1);
-                t[(v + NBUF - 1) % NBUF].load(kpool + off, vpool + off, r, g);
-                o.step<KV>(t[v], q, scale, t0 + j * kBS + 4 * g, t1, t0 + (j + 1) * kBS);
+        issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
+        if (first) {
+            piece_end = crb1 < u1 ? crb1 : u1;
+            t1 = min(c_len, (p.prefix_blocks + static_cast<int>(piece_end - crb0)) * kBS);
+            pbad = false;
+            o = Online();
+            if (p.prefix_blocks > 0 && x == crb0) {
+                // the row's first piece starts from its state over the shared
+                // prefix, the states of the prefix's key ranges combined (one
+                // lane group carries the normaliser)
+                o.m = prefix_state(p, qrow_of(bc), g, o.acc, o.l);
             }
         }
-
-        float l = o.l;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const bool whole = rb0 >= u0 && rb1 <= u1;  // no other wavefront touches this row
-        if (head_ok) {
-            if (whole) {
-                const float inv = bad ? nan : vs / l;
+        pbad = pbad || tb;
+        const int tok0 = (p.prefix_blocks + static_cast<int>(x - crb0)) * kBS;
+        o.step<KV>(cur, q, scale, tok0 + 4 * g, t1, tok0 + kBS);
+        if (x + 1 == piece_end) {  // last block of the piece: write it
+            float l = o.l;
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const bool whole = crb0 >= u0 && crb1 <= u1;  // no other wavefront touches this row
+            if (head_ok) {
+                const int64_t qrow = qrow_of(bc);
+                if (whole) {
+                    const float inv = pbad ? nan : vs / l;
 #pragma unroll
-                for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, o.acc[n] * inv);
-            } else {
-                const int side = (b == b_first) ? 0 : 1;
-                const int64_t w = ((static_cast<int64_t>(kvh) * p.parts + wi) * 2 + side) * p.group + r;
+                    for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, o.acc[n] * inv);
+                } else {
+                    const int side = (bc == b_first) ? 0 : 1;
+                    const int64_t w = ((static_cast<int64_t>(kvh) * p.parts + wi) * 2 + side) * p.group + r;
 #pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    st<f32x4_t>(p.ws_acc + w * kD + 16 * n + 4 * g, bad ? nan4 : o.acc[n] * vs);
-                if (g == 0) st<float2>(p.ws_ml + 2 * w, float2{o.m, bad ? nan : l});
+                    for (int n = 0; n < 8; ++n)
+                        st<f32x4_t>(p.ws_acc + w * kD + 16 * n + 4 * g, pbad ? nan4 : o.acc[n] * vs);
+                    if (g == 0) st<float2>(p.ws_ml + 2 * w, float2{o.m, pbad ? nan : l});
+                }
             }
         }
-        u = rb1 < u1 ? rb1 : u1;
+    };
+
+    // two blocks per trip, so the ring slots are fixed registers
+    for (int64_t x = u0; x < u1; x += 2) {
+        step(t[0], tbad[0], t[1], tbad[1], x);
+        if (x + 1 >= u1) break;
+        step(t[1], tbad[1], t[0], tbad[0], x + 1);
     }
 }
 
@@ -717,27 +809,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
 #undef PKV_MERGE_SLOT
 }
 
-// Blocks in flight per wavefront (2..4).  PKV_DECODE_DEPTH overrides the
-// default for tuning runs.
-int decode_pipeline_depth() {
-    static const int depth = [] {
-        const char* e = std::getenv("PKV_DECODE_DEPTH");
-        const int v = e ? std::atoi(e) : 2;
-        return v < 2 ? 2 : (v > 4 ? 4 : v);
-    }();
-    return depth;
-}
-
-// Wavefronts per kv head: PKV_DECODE_WAVES_PER_CU wavefronts per compute
-// unit in total (default 8; 12 for a one-byte cache, whose blocks carry half
-// the bytes for the same instruction count), shared among the kv heads.
+// Wavefronts per kv head: eight per CU over all CUs (the decode kernel's
+// registers allow two wavefronts per SIMD for every cache type; fp32 caches
+// fit one).  PKV_DECODE_WAVES_PER_CU overrides the eight for tuning runs.
 int decode_parts_auto(int hkv, int kv_dtype) {
+    (void)kv_dtype;
     static const int env = [] {
         const char* e = std::getenv("PKV_DECODE_WAVES_PER_CU");
         const int v = e ? std::atoi(e) : 0;
         return v < 0 ? 0 : (v > 32 ? 32 : v);
     }();
-    const int per_cu = env > 0 ? env : (is_byte_dtype(kv_dtype) ? 12 : 8);
+    const int per_cu = env > 0 ? env : 8;
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -749,23 +831,19 @@ int decode_parts_auto(int hkv, int kv_dtype) {
 }
 
 template <bool LOCAL>
-void launch_decode_kernel(int kv_dtype, int depth, dim3 grid, hipStream_t stream, const DecodeParams& p) {
+void launch_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const DecodeParams& p) {
     switch (kv_dtype) {
         case PKV_F32:
-            hipLaunchKernelGGL((decode_kernel<PKV_F32, 2, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
-            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 2, LOCAL>), grid, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_BF16, 3, LOCAL>), grid, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_kernel<PKV_BF16, 4, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_FP8_E4M3:
-            if (depth <= 2) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 2, LOCAL>), grid, dim3(64), 0, stream, p);
-            else if (depth == 3) hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 3, LOCAL>), grid, dim3(64), 0, stream, p);
-            else hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, 4, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL((decode_kernel<PKV_INT8, 2, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL>), grid, dim3(64), 0, stream, p);
             break;
     }
 }
@@ -851,11 +929,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
         if (st) return st;
     }
     const dim3 g1(static_cast<unsigned>(grid));
-    const int depth = decode_pipeline_depth();
     if (local)
-        launch_decode_kernel<true>(c->kv_dtype, depth, g1, stream, p);
+        launch_decode_kernel<true>(c->kv_dtype, g1, stream, p);
     else
-        launch_decode_kernel<false>(c->kv_dtype, depth, g1, stream, p);
+        launch_decode_kernel<false>(c->kv_dtype, g1, stream, p);
     mark(1);
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads));
     if (f32)
