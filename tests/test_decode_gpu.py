@@ -64,6 +64,8 @@ def test_shared_prefix_bf16_with_one_copy_on_write(variant):
     rng = np.random.default_rng(0)
     rows = sorted(set([0, 1, 2, 3, 253, 254, 255] + rng.integers(0, 256, 25).tolist()))
     check_decode(w, rows=rows, hip=hip)
+    # the same batch with the shared-prefix promise, as the benchmark runs it
+    check_decode(w, rows=rows, hip=hip, shared_prefix_blocks=125)
 
 
 @pytest.mark.parametrize("variant", ["plain", "needle"])
@@ -78,6 +80,13 @@ def test_int8_long_context(variant):
     w = W.int8_long(variant=variant, batch=4, length=65536)
     heads = list(range(0, 8)) + list(range(56, 64))
     check_decode(w, rows=[0, 3], heads=heads)
+
+
+def test_int8_long_context_full_size():
+    """The benchmark's int8 batch at its full size (16 rows of 131072 tokens),
+    sampled rows and heads."""
+    w = W.int8_long(variant="needle")
+    check_decode(w, rows=[0, 15], heads=[0, 9, 63])
 
 
 EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025, 2047, 4097]
