@@ -672,14 +672,15 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 // Merge the pieces of one (row, query head) that was divided between
 // wavefronts: out = sum_i acc_i 2^(m_i - M) / sum_i l_i 2^(m_i - M),
 // M = max_i m_i, in wavefront order.  The pieces are read kMergeBatch at a
-// time (indices past the last piece repeat it and are left out of the sums).
+// time (indices past the last piece repeat it and are left out of the sums);
+// past the first batch the sums are rescaled whenever the maximum moves.
 constexpr int kMaxParts = 4096;
 constexpr int kMergeBatch = 8;
-// One wavefront per (row, kv head); lane l owns d = 2 l, 2 l + 1 of every
-// query head of the group.  The row's plan and wavefront range are worked out
-// once; then, for kMergeHeads heads at a time, the pieces are read with every
-// load of a batch issued together, so a row cut into at most kMergeBatch
-// pieces costs one round of loads per kMergeHeads heads after the plan's.
+// One wavefront per (row, kv head, group of kMergeHeads query heads); lane l
+// owns d = 2 l, 2 l + 1 of those heads.  The row's plan and wavefront range
+// are worked out once; then every load of a batch is issued together, so a
+// row cut into at most kMergeBatch pieces costs one round of loads after the
+// plan's.
 constexpr int kMergeHeads = 4;
 
 template <int QT>
@@ -693,10 +694,16 @@ __device__ __forceinline__ void store_out2(void* out, int64_t qrow, int d, float
 
 template <int QT>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) {
-    const int b = static_cast<int>(blockIdx.x / p.hkv);
+    // kv head fastest, as in the decode kernel, so a head's partial results
+    // are read on the XCD that wrote them
+    const int hgroups = (p.group + kMergeHeads - 1) / kMergeHeads;
     const int kvh = static_cast<int>(blockIdx.x % p.hkv);
+    const int rest = static_cast<int>(blockIdx.x / p.hkv);
+    const int h0 = (rest % hgroups) * kMergeHeads;
+    const int b = rest / hgroups;
     const int d = 2 * threadIdx.x;
     const int grp = p.group;
+    const int nh = min(kMergeHeads, grp - h0);  // heads of this wavefront
     const int64_t row_q = static_cast<int64_t>(b) * p.hq + kvh * grp;  // query row of head 0 of the group
     const int64_t U = p.plan[p.rows];
     const int64_t rb0 = p.plan[b];
@@ -707,7 +714,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
         if (p.prefix_blocks > 0 && row_valid(p.kv_lens[b], p)) {
             const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
             const float vs = p.byte_kv ? p.v_scale[kvh] : 1.f;
-            for (int hh = 0; hh < grp; ++hh) {
+            for (int hh = h0; hh < h0 + nh; ++hh) {
                 const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
                 float mx = -INFINITY;
                 for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
@@ -746,66 +753,56 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
     const int64_t base0 = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp;
     // slot of (head hh, piece k), the piece clamped to the last one
 #define PKV_MERGE_SLOT(hh, k) (base0 + (hh) + (2 * min((k), n - 1) + ((k) == 0 ? side0 : 0)) * grp)
-    for (int h0 = 0; h0 < grp; h0 += kMergeHeads) {
-        float mx[kMergeHeads];
-        float2 num[kMergeHeads];
-        float den[kMergeHeads];
+    float mx[kMergeHeads];
+    float2 num[kMergeHeads];
+    float den[kMergeHeads];
+#pragma unroll
+    for (int a = 0; a < kMergeHeads; ++a) {
+        mx[a] = -INFINITY;
+        num[a] = float2{0.f, 0.f};
+        den[a] = 0.f;
+    }
+    float2 ml[kMergeHeads][kMergeBatch];
+    float2 acc[kMergeHeads][kMergeBatch];
+    for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
 #pragma unroll
         for (int a = 0; a < kMergeHeads; ++a) {
-            mx[a] = -INFINITY;
-            num[a] = float2{0.f, 0.f};
-            den[a] = 0.f;
+            const int hh = h0 + min(a, nh - 1);
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const int64_t sl = PKV_MERGE_SLOT(hh, k0 + j);
+                ml[a][j] = ld<float2>(ws_ml + 2 * sl);
+                acc[a][j] = ld<float2>(ws_acc + sl * kD + d);
+            }
         }
-        // first pass: the running max (one batch of loads when n <= kMergeBatch)
-        float2 ml[kMergeHeads][kMergeBatch];
-        float2 acc[kMergeHeads][kMergeBatch];
-        for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+        // every load of the batch is in flight before the first is used
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int a = 0; a < kMergeHeads; ++a) {
-                const int hh = min(h0 + a, grp - 1);
+        for (int a = 0; a < kMergeHeads; ++a) {
+            float bm = mx[a];
 #pragma unroll
-                for (int j = 0; j < kMergeBatch; ++j) {
-                    const int64_t sl = PKV_MERGE_SLOT(hh, k0 + j);
-                    ml[a][j] = ld<float2>(ws_ml + 2 * sl);
-                    acc[a][j] = ld<float2>(ws_acc + sl * kD + d);
-                }
+            for (int j = 0; j < kMergeBatch; ++j) bm = fmaxf(bm, ml[a][j].x);  // repeats are real pieces
+            if (bm > mx[a]) {  // the maximum moved: rescale what is summed (nothing in the first batch)
+                const float r = mx[a] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx[a] - bm);
+                num[a].x *= r;
+                num[a].y *= r;
+                den[a] *= r;
+                mx[a] = bm;
             }
 #pragma unroll
-            for (int a = 0; a < kMergeHeads; ++a)
-#pragma unroll
-                for (int j = 0; j < kMergeBatch; ++j) mx[a] = fmaxf(mx[a], ml[a][j].x);  // repeats are real pieces
-        }
-        // second pass: the weighted sums, in piece order (the loads of a row
-        // cut into at most kMergeBatch pieces are still in registers)
-        for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
-            if (n > kMergeBatch) {
-#pragma unroll
-                for (int a = 0; a < kMergeHeads; ++a) {
-                    const int hh = min(h0 + a, grp - 1);
-#pragma unroll
-                    for (int j = 0; j < kMergeBatch; ++j) {
-                        const int64_t sl = PKV_MERGE_SLOT(hh, k0 + j);
-                        ml[a][j] = ld<float2>(ws_ml + 2 * sl);
-                        acc[a][j] = ld<float2>(ws_acc + sl * kD + d);
-                    }
+            for (int j = 0; j < kMergeBatch; ++j) {
+                if (k0 + j < n) {
+                    const float w = __builtin_amdgcn_exp2f(ml[a][j].x - mx[a]);
+                    num[a].x += acc[a][j].x * w;
+                    num[a].y += acc[a][j].y * w;
+                    den[a] += ml[a][j].y * w;
                 }
             }
-#pragma unroll
-            for (int a = 0; a < kMergeHeads; ++a)
-#pragma unroll
-                for (int j = 0; j < kMergeBatch; ++j) {
-                    if (k0 + j < n) {
-                        const float w = __builtin_amdgcn_exp2f(ml[a][j].x - mx[a]);
-                        num[a].x += acc[a][j].x * w;
-                        num[a].y += acc[a][j].y * w;
-                        den[a] += ml[a][j].y * w;
-                    }
-                }
         }
-#pragma unroll
-        for (int a = 0; a < kMergeHeads; ++a)
-            if (h0 + a < grp) store_out2<QT>(p.out, row_q + h0 + a, d, num[a].x / den[a], num[a].y / den[a]);
     }
+#pragma unroll
+    for (int a = 0; a < kMergeHeads; ++a)
+        if (a < nh) store_out2<QT>(p.out, row_q + h0 + a, d, num[a].x / den[a], num[a].y / den[a]);
 #undef PKV_MERGE_SLOT
 }
 
@@ -934,7 +931,8 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     else
         launch_decode_kernel<false>(c->kv_dtype, g1, stream, p);
     mark(1);
-    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads));
+    const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + kMergeHeads - 1) / kMergeHeads;
+    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads * hgroups));
     if (f32)
         hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, dim3(64), 0, stream, p);
     else
