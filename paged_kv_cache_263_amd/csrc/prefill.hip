@@ -35,6 +35,8 @@
 // per-head scales folded into the score scale and the output.
 #include <cmath>
 
+#include <cstdlib>
+
 #include "device.h"
 #include "internal.h"
 
@@ -395,13 +397,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
 }  // namespace
 
-// Key ranges the shared-prefix pass splits into: enough workgroups for two
-// per compute unit, each range at least one 64-key iteration, at most 8.
+// Key ranges the shared-prefix pass splits into: enough workgroups for one
+// per compute unit (measured on 256 rows: two ranges beat four by 5 us, as
+// each range's states are written and combined), each range at least one
+// 64-key iteration, at most 8.
 int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {
     const int32_t group = a->num_q_heads / c->num_kv_heads;
     const int64_t tiles = static_cast<int64_t>((rows + kRows / group - 1) / (kRows / group)) * c->num_kv_heads;
     const int64_t iters = (static_cast<int64_t>(a->shared_prefix_blocks) * kBS + kKeys - 1) / kKeys;
-    int64_t parts = (512 + tiles - 1) / tiles;
+    static const int env = [] {  // PKV_PREFIX_PARTS overrides the count for tuning runs
+        const char* e = std::getenv("PKV_PREFIX_PARTS");
+        return e ? std::atoi(e) : 0;
+    }();
+    int64_t parts = env > 0 ? env : (256 + tiles - 1) / tiles;
     parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
     return static_cast<int>(parts < iters ? parts : (iters < 1 ? 1 : iters));
 }
