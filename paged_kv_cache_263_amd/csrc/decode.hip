@@ -147,11 +147,16 @@ struct Tile<PKV_BF16> {
             q[ks] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
+    // Streaming (non-temporal) loads: a decode step reads each tile once, and
+    // with this policy on both K and V the kernel reads the Llama-shaped
+    // batch about 10% faster (K alone or V alone gain less).  The one-byte
+    // tiles below use it too; it pays only where each load instruction of a
+    // wave covers whole 64-byte pieces of the tile.
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) k[ks] = ld<u32x4_t>(kt + r * kD + 32 * ks + 8 * g);
+        for (int ks = 0; ks < 4; ++ks) k[ks] = ld_stream<u32x4_t>(kt + r * kD + 32 * ks + 8 * g);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) v[n] = ld<u32x2_t>(vt + (16 * n + r) * kBS + 4 * g);
+        for (int n = 0; n < 8; ++n) v[n] = ld_stream<u32x2_t>(vt + (16 * n + r) * kBS + 4 * g);
     }
     // Zero this lane's V elements of tokens 4g + i with keep[i] false (the
     // unwritten tail of a block may hold any bits, and 0 * NaN is NaN).
@@ -181,30 +186,32 @@ struct Tile<PKV_BF16> {
 };
 
 // One-byte (fp8, int8) tiles are read with 16-byte loads (narrower loads cap
-// the read rate well below the HBM rate).  K: lane (r, g) reads codes 32 g ..
-// 32 g + 31 of token row r, and matrix step ks takes codes 32 g + 8 ks .. +7;
-// the query
+// the read rate well below the HBM rate), laid out so that every load
+// instruction of a wave reads whole 64-byte pieces of the tile.  K: lane
+// (r, g) reads codes 64 s + 16 g .. +15 of token row r for s = 0, 1, and
+// matrix step ks takes codes 64 (ks / 2) + 16 g + 8 (ks % 2) .. +7; the query
 // operand uses the same order of d (a permutation of the contraction index,
 // so the scores are unchanged).  V: the tile layout of byte_v_offset puts the
-// lane's 8 words (tokens 4g..4g+3 of d rows 16 n + r) in 32 contiguous bytes.
+// lane's 8 words (tokens 4g..4g+3 of d rows 16 n + r) in two 16-byte pieces.
 template <int KV>
 struct ByteTile {
     using Elt = uint8_t;
     using Q = bf16x8_t[4];
-    u32x4_t k[2];  // codes 32 g .. 32 g + 31 of token row r
+    u32x4_t k[2];  // codes 64 s + 16 g .. +15 of token row r
     u32x4_t v[2];  // word n: tokens 4g..4g+3 of d row 16 n + r
     static __device__ __forceinline__ void load_q(Q& q, const void* qp, bool ok, int g) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t x = ok ? ld<u32x4_t>(static_cast<const uint16_t*>(qp) + 32 * g + 8 * ks) : u32x4_t{0, 0, 0, 0};
+            u32x4_t x = ok ? ld<u32x4_t>(static_cast<const uint16_t*>(qp) + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1))
+                           : u32x4_t{0, 0, 0, 0};
             q[ks] = __builtin_bit_cast(bf16x8_t, x);
         }
     }
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) k[s] = ld<u32x4_t>(kt + r * kD + 32 * g + 16 * s);
+        for (int s = 0; s < 2; ++s) k[s] = ld_stream<u32x4_t>(kt + r * kD + 64 * s + 16 * g);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) v[s] = ld<u32x4_t>(vt + g * 512 + r * 32 + 16 * s);
+        for (int s = 0; s < 2; ++s) v[s] = ld_stream<u32x4_t>(vt + g * 512 + s * 256 + r * 16);
     }
     __device__ __forceinline__ void mask_v(const bool keep[4]) {
         const uint32_t m = (keep[0] ? 0xFFu : 0u) | (keep[1] ? 0xFF00u : 0u) | (keep[2] ? 0xFF0000u : 0u) |

@@ -25,6 +25,13 @@ template <typename T>
 __device__ __forceinline__ T ld(const void* p) {
     return *static_cast<const T*>(p);
 }
+// A load marked non-temporal (the `nt` cache policy): data read once per
+// call, such as the K/V tiles a decode step streams, so the caches treat it
+// as streaming rather than keeping it at the expense of other lines.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const T*>(p));
+}
 template <typename T>
 __device__ __forceinline__ void st(void* p, T v) {
     *static_cast<T*>(p) = v;
@@ -80,13 +87,14 @@ __device__ __forceinline__ u32x2_t byte4_to_bf16x4(uint32_t w) {
 }
 
 // Byte offset of (d row, token) inside a one-byte (fp8 or int8) V tile
-// (2 KiB): tokens in
-// groups of 4, then d % 16, then d / 16, then the token within its group.
-// Lane (r, g) of the decode kernel then finds the 8 words it feeds to the
-// matrix cores - tokens 4g..4g+3 of d rows 16 n + r, n = 0..7 - in 32
-// contiguous bytes at g * 512 + r * 32, read as two 16-byte loads.
+// (2 KiB): tokens in groups of 4, then d / 64, then d % 16, then (d / 16) % 4,
+// then the token within its group.  Lane (r, g) of the decode kernel then
+// finds the 8 words it feeds to the matrix cores - tokens 4g..4g+3 of d rows
+// 16 n + r, n = 0..7 - as two 16-byte pieces at g * 512 + s * 256 + r * 16
+// (words n = 4 s .. 4 s + 3), so each of its two load instructions reads
+// whole 256-byte runs of the tile.
 __device__ __forceinline__ int byte_v_offset(int d, int tok) {
-    return (tok >> 2) * 512 + (d & 15) * 32 + (d >> 4) * 4 + (tok & 3);
+    return (tok >> 2) * 512 + (d >> 6) * 256 + (d & 15) * 16 + ((d >> 4) & 3) * 4 + (tok & 3);
 }
 
 // fp32 -> E4M3 code: nearest, ties to even mantissa, |x| >= 448 saturates to

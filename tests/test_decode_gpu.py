@@ -113,7 +113,7 @@ def test_one_byte_codes_bit_exact(kv):
     lens, starts = W.replay_lengths(w)
     kp = hip.cache.k_pool[0].cpu().view(torch.uint8).numpy()  # [NB, hkv, 16, 128]
     # one-byte V tiles (2 KiB per block and kv head): (d, token) at byte
-    # (token // 4) * 512 + (d % 16) * 32 + (d // 16) * 4 + token % 4
+    # (token // 4) * 512 + (d // 64) * 256 + (d % 16) * 16 + ((d // 16) % 4) * 4 + token % 4
     vp = hip.cache.v_pool[0].cpu().view(torch.uint8).numpy().reshape(w.num_blocks, w.hkv, 2048)
     dd = np.arange(128)
     for op in w.script:
@@ -125,7 +125,8 @@ def test_one_byte_codes_bit_exact(kv):
         blk, off = row[t // 16], t % 16
         for j in range(w.hkv):
             gk = kp[blk, j, off, :]
-            vidx = (off[:, None] // 4) * 512 + (dd[None, :] % 16) * 32 + (dd[None, :] // 16) * 4 + off[:, None] % 4
+            vidx = ((off[:, None] // 4) * 512 + (dd[None, :] // 64) * 256 + (dd[None, :] % 16) * 16
+                    + ((dd[None, :] // 16) % 4) * 4 + off[:, None] % 4)
             gv = vp[blk[:, None], j, vidx]
             ok = codec.quantise_scaled(k[:, j].float().cpu().numpy(), w.k_scale[j]).view(np.uint8)
             ov = codec.quantise_scaled(v[:, j].float().cpu().numpy(), w.v_scale[j]).view(np.uint8)
