@@ -813,17 +813,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
 #undef PKV_MERGE_SLOT
 }
 
-// Wavefronts per kv head: eight per CU over all CUs (the decode kernel's
-// registers allow two wavefronts per SIMD for every cache type; fp32 caches
-// fit one).  PKV_DECODE_WAVES_PER_CU overrides the eight for tuning runs.
+// Wavefronts per kv head, as a count per CU over all CUs: four (one per
+// SIMD) for bf16 caches, eight for the others.  These are the measured best
+// under streaming tile loads: bf16 decode of the Llama-shaped batch takes
+// 190 us at four per CU, 194-196 at eight and 198-199 at five (an uneven
+// share of the SIMDs); one-byte caches need eight wavefronts in flight (669 us
+// against 779 at four on the long-context fp8 batch).  The registers allow
+// two wavefronts per SIMD for every cache type but fp32, which fits one.
+// PKV_DECODE_WAVES_PER_CU overrides the default for tuning runs.
 int decode_parts_auto(int hkv, int kv_dtype) {
-    (void)kv_dtype;
     static const int env = [] {
         const char* e = std::getenv("PKV_DECODE_WAVES_PER_CU");
         const int v = e ? std::atoi(e) : 0;
         return v < 0 ? 0 : (v > 32 ? 32 : v);
     }();
-    const int per_cu = env > 0 ? env : 8;
+    const int per_cu = env > 0 ? env : (kv_dtype == PKV_BF16 ? 4 : 8);
     static const int cus = [] {
         int dev = 0, n = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
