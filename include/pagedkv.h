@@ -213,7 +213,12 @@ int block_table_build(const pkv_pool* pool, const int32_t* seqs, int32_t n, int3
  * tokens reads contiguous memory.)  One-byte V tiles (fp8 and int8: 16 x 128
  * codes, 2 KiB) keep (d, token) at byte (token / 4) * 512 + (d / 64) * 256 +
  * (d % 16) * 16 + ((d / 16) % 4) * 4 + token % 4, so the decode kernel reads
- * them with 16-byte loads that cover whole 256-byte runs.  Elements are kv_dtype.  Stored value = e4m3(code) * scale for fp8
+ * them with 16-byte loads that cover whole 256-byte runs.  bf16 tiles (4 KiB)
+ * keep K (token, d) at element (d / 8) * 128 + token * 8 + d % 8 and V
+ * (d, token) at element (d / 32) * 512 + ((token / 4) * 16 + d % 16) * 8 +
+ * ((d / 16) % 2) * 4 + token % 4, so every load instruction of the decode
+ * kernel reads 1 KiB contiguously.  fp32 tiles keep the plain orders above.
+ * Only the library's kernels read or write inside a tile.  Elements are kv_dtype.  Stored value = e4m3(code) * scale for fp8
  * ([P2] "Quantising the cache") and code * scale for int8 (a signed byte in
  * -127..127; [P3] "M.65 Inference Serving", quantisation of the KV cache),
  * with one fp32 scale per (layer, kv head) for K (k_scale [num_layers]

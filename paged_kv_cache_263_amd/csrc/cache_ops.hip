@@ -36,8 +36,8 @@ struct WriteParams {
 };
 
 // Four consecutive d of one head of one token: the values as read, and
-// their stores into the K tile ([16][128]) and the V tile ([128][16]; fp8:
-// byte_v_offset).
+// their stores into the K tile ([16][128]; bf16: bf16_k_offset) and the V
+// tile ([128][16]; bf16: bf16_v_offset; one-byte caches: byte_v_offset).
 template <int KV>
 struct Quad {
     // one-byte code of a value already divided by its scale
@@ -66,9 +66,9 @@ struct Quad {
         } else if constexpr (KV == PKV_BF16) {
             uint16_t* kp = static_cast<uint16_t*>(p.k_pool) + tile;
             uint16_t* vp = static_cast<uint16_t*>(p.v_pool) + tile;
-            st<u32x2_t>(kp + o * kD + d, k);
+            st<u32x2_t>(kp + bf16_k_offset(o, d), k);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vp[(d + j) * kBS + o] = static_cast<uint16_t>(v[j >> 1] >> (16 * (j & 1)));
+            for (int j = 0; j < 4; ++j) vp[bf16_v_offset(d + j, o)] = static_cast<uint16_t>(v[j >> 1] >> (16 * (j & 1)));
         } else {
             uint8_t* kp = static_cast<uint8_t*>(p.k_pool) + tile;
             uint8_t* vp = static_cast<uint8_t*>(p.v_pool) + tile;

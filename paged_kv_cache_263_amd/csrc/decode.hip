@@ -152,11 +152,18 @@ struct Tile<PKV_BF16> {
     // batch about 10% faster (K alone or V alone gain less).  The one-byte
     // tiles below use it too; it pays only where each load instruction of a
     // wave covers whole 64-byte pieces of the tile.
+    // The tile orders of bf16_k_offset and bf16_v_offset make each load
+    // instruction read 1 KiB of the tile contiguously.
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
+        const int lane = 16 * g + r;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) k[ks] = ld_stream<u32x4_t>(kt + r * kD + 32 * ks + 8 * g);
+        for (int ks = 0; ks < 4; ++ks) k[ks] = ld_stream<u32x4_t>(kt + 512 * ks + 8 * lane);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) v[n] = ld_stream<u32x2_t>(vt + (16 * n + r) * kBS + 4 * g);
+        for (int m = 0; m < 4; ++m) {
+            const u32x4_t w = ld_stream<u32x4_t>(vt + 512 * m + 8 * lane);  // d rows 16 (2m) + r, 16 (2m + 1) + r
+            v[2 * m] = u32x2_t{w[0], w[1]};
+            v[2 * m + 1] = u32x2_t{w[2], w[3]};
+        }
     }
     // Zero this lane's V elements of tokens 4g + i with keep[i] false (the
     // unwritten tail of a block may hold any bits, and 0 * NaN is NaN).

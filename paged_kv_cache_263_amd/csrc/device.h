@@ -86,6 +86,23 @@ __device__ __forceinline__ u32x2_t byte4_to_bf16x4(uint32_t w) {
     else return fp8x4_to_bf16x4(w);
 }
 
+// Element offset of (token, d) inside a bf16 K tile (16 tokens x 128 d,
+// 4 KiB): 16-byte pieces of 8 consecutive d, ordered by d / 8, then token.
+// Lane 16 g + r of the decode kernel feeds matrix step ks with token r, d
+// 32 ks + 8 g .. +7 - piece 64 ks + 16 g + r - so each of its four load
+// instructions reads 1 KiB of the tile contiguously; the prefill kernel's
+// thread t stages piece t.
+__device__ __forceinline__ int bf16_k_offset(int tok, int d) { return (d >> 3) * 128 + tok * 8 + (d & 7); }
+
+// Element offset of (d row, token) inside a bf16 V tile (128 d x 16 tokens):
+// with d = 16 n + r, n = 2 m + h and token = 4 g + i, at m * 512 +
+// (16 g + r) * 8 + h * 4 + i.  Decode lane 16 g + r feeds the matrix cores
+// tokens 4g..4g+3 of d rows 16 n + r, n = 0..7; piece m of that lane holds
+// n = 2 m and 2 m + 1, so its four loads read 1 KiB contiguously each.
+__device__ __forceinline__ int bf16_v_offset(int d, int tok) {
+    return (d >> 5) * 512 + ((tok >> 2) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (tok & 3);
+}
+
 // Byte offset of (d row, token) inside a one-byte (fp8 or int8) V tile
 // (2 KiB): tokens in groups of 4, then d / 64, then d % 16, then (d / 16) % 4,
 // then the token within its group.  Lane (r, g) of the decode kernel then

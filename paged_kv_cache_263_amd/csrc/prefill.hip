@@ -90,9 +90,12 @@ constexpr int kPrefixState = kD + 4;
 __device__ __forceinline__ int v_lds_offset(int d, int h) { return d * kBS + 8 * (h ^ ((d >> 3) & 1)); }
 
 // Staging registers for one iteration: thread t owns 16 bytes of each of the
-// iteration's 4 K tiles (row t/16, elements (t%16)*8..+7) and 4 V tiles
-// (d row t/2, tokens (t%2)*8..+7); one-byte codes are converted to bf16 on
-// load.
+// iteration's 4 K tiles and 4 V tiles.  bf16 tiles: piece t of the tile
+// (bf16_k_offset, bf16_v_offset), so 256 threads read each 4 KiB tile
+// contiguously; K piece t is token t%16, d 8(t/16)..+7, and V piece t holds
+// tokens 4g..4g+3 (g = (t/16)%4) of d rows 32(t/64) + t%16 and that + 16.
+// One-byte tiles: K row t/16, elements (t%16)*8..+7, and V d row t/2, tokens
+// (t%2)*8..+7, their codes converted to bf16 on load.
 // The tile addresses are uniform (one per block) and the thread's offset
 // inside a tile is fixed, so a load costs no vector arithmetic.
 template <int KV>
@@ -121,21 +124,32 @@ struct Stage {
     // blocks past its end, which hold whatever the clamped load read; 0 * NaN
     // is NaN).  Only the iteration that reaches the row's end calls this.
     __device__ __forceinline__ void mask_tail(const int valid[4], int t) {
-        const int tok0 = (t & 1) * 8;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (tok0 + e >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            for (int e = 0; e < 8; ++e) {
+                // token of element e
+                const int tok = KV == PKV_BF16 ? 4 * ((t >> 4) & 3) + (e & 3) : (t & 1) * 8 + e;
+                if (tok >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            }
             v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
     }
     __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs, int t) const {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            st<u32x4_t>(ks + (b * kBS + (t >> 4)) * kKStride + (t & 15) * 8, k[b]);
-            st<u32x4_t>(vs + b * kTile + v_lds_offset(t >> 1, t & 1), v[b]);
+            if constexpr (KV == PKV_BF16) {
+                st<u32x4_t>(ks + (b * kBS + (t & 15)) * kKStride + 8 * (t >> 4), k[b]);
+                const int g = (t >> 4) & 3;
+                const int d0 = 32 * (t >> 6) + (t & 15);
+                uint16_t* vt = vs + b * kTile + 4 * (g & 1);
+                st<u32x2_t>(vt + v_lds_offset(d0, g >> 1), u32x2_t{v[b][0], v[b][1]});
+                st<u32x2_t>(vt + v_lds_offset(d0 + 16, g >> 1), u32x2_t{v[b][2], v[b][3]});
+            } else {
+                st<u32x4_t>(ks + (b * kBS + (t >> 4)) * kKStride + (t & 15) * 8, k[b]);
+                st<u32x4_t>(vs + b * kTile + v_lds_offset(t >> 1, t & 1), v[b]);
+            }
         }
     }
 };
@@ -226,9 +240,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
     const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
-    const uint32_t koff = static_cast<uint32_t>(((t >> 4) * kD + (t & 15) * 8) * kElt);
-    const uint32_t voff = static_cast<uint32_t>(
-        KV == PKV_BF16 ? ((t >> 1) * kBS + (t & 1) * 8) * kElt : byte_v_offset(t >> 1, (t & 1) * 8));
+    const uint32_t koff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : ((t >> 4) * kD + (t & 15) * 8) * kElt);
+    const uint32_t voff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : byte_v_offset(t >> 1, (t & 1) * 8));
     const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(t >> 1, (t & 1) * 8 + 4));
     // LDS element offsets of this lane's operands
     const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
