@@ -250,7 +250,7 @@ typedef struct {
     const int32_t* block_table;  /* device [num_seqs][max_blocks], row i for batch row i */
     int32_t max_blocks;
     const int32_t* kv_lens;      /* device [num_seqs]: cached tokens per row, >= 1 */
-    int32_t max_kv_len;          /* host: upper bound on kv_lens (sizes the launch) */
+    int32_t max_kv_len;          /* host: upper bound on kv_lens (sizes the launch); num_seqs x ceil(max_kv_len / 16) must be below 2^31 (PKV_ERR_INVALID otherwise) */
     /* prefill only (paged_attn_prefill_chunk): */
     const int32_t* cu_q;         /* device [num_seqs + 1]: row i's queries are cu_q[i]..cu_q[i+1]-1 */
     int32_t num_decode;          /* rows 0..num_decode-1 have exactly one query (cu_q[i] = i) */

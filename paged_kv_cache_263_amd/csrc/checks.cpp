@@ -46,6 +46,10 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
         return fail(PKV_ERR_INVALID, "max_blocks %d / max_kv_len %d must be positive", a->max_blocks, a->max_kv_len);
     if (static_cast<int64_t>(a->max_kv_len) > static_cast<int64_t>(a->max_blocks) * PKV_BLOCK_SIZE)
         return fail(PKV_ERR_INVALID, "max_kv_len %d exceeds max_blocks * 16", a->max_kv_len);
+    // the kernels sum block counts over rows in 32 bits
+    if (static_cast<int64_t>(a->num_seqs) * ((a->max_kv_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE) > INT32_MAX)
+        return fail(PKV_ERR_INVALID, "num_seqs %d x ceil(max_kv_len %d / 16) blocks exceeds 2^31 - 1", a->num_seqs,
+                    a->max_kv_len);
     if (a->decode_parts < 0 || a->decode_parts > 4096)
         return fail(PKV_ERR_INVALID, "decode_parts %d must be in [0, 4096]", a->decode_parts);
     const uintptr_t align = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->out) |

@@ -45,6 +45,7 @@
 // output.
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -94,7 +95,8 @@ __device__ __forceinline__ int suffix_blocks(int L, const DecodeParams& p) {
 }
 
 // First block of wavefront i's range for a head with U blocks over Q parts.
-__device__ __forceinline__ int64_t range_start(int64_t U, int i, int Q) { return U * i / Q; }
+// (U < 2^31, checked on the host, so the result fits 32 bits.)
+__device__ __forceinline__ int range_start(int64_t U, int i, int Q) { return static_cast<int>(U * i / Q); }
 
 // Parts actually used: at most one per kMinBlocks blocks, so that no range is
 // empty (every wavefront that has a range writes its pieces) and tiny batches
@@ -114,6 +116,22 @@ __device__ __forceinline__ void store_out4(void* out, int64_t qrow, int d, f32x4
         const uint32_t b = bf16_bits_rne(v[2]) | (bf16_bits_rne(v[3]) << 16);
         st<u32x2_t>(static_cast<uint16_t*>(out) + qrow * kD + d, u32x2_t{a, b});
     }
+}
+
+// Buffer descriptor of one tile (a raw buffer of `bytes` bytes from the
+// tile's start), built in scalar registers from the wave-uniform tile
+// address.  Loads through it take the lane's fixed 32-bit byte offset, so a
+// block costs no vector address arithmetic: a 64-bit vector address per block
+// could be placed in registers that an in-flight tile load still targets,
+// and the wave would then wait for that load before issuing the next tile.
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, no swizzle
+constexpr int kLoadStream = 2;          // cache policy: non-temporal (nt)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* tile, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(tile);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), bytes, kRsrcWord3);
 }
 
 // Split p into bf16 high and low parts packed as the B operand (4 tokens).
@@ -154,13 +172,18 @@ struct Tile<PKV_BF16> {
     // wave covers whole 64-byte pieces of the tile.
     // The tile orders of bf16_k_offset and bf16_v_offset make each load
     // instruction read 1 KiB of the tile contiguously.
+    // Buffer loads through per-tile descriptors (tile_rsrc).
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
-        const int lane = 16 * g + r;
+        const int lane_off = 16 * (16 * g + r);
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kt, kTile * 2);
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(vt, kTile * 2);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) k[ks] = ld_stream<u32x4_t>(kt + 512 * ks + 8 * lane);
+        for (int ks = 0; ks < 4; ++ks)
+            k[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, lane_off + 1024 * ks, 0, kLoadStream);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const u32x4_t w = ld_stream<u32x4_t>(vt + 512 * m + 8 * lane);  // d rows 16 (2m) + r, 16 (2m + 1) + r
+            // d rows 16 (2m) + r and 16 (2m + 1) + r
+            const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(vr, lane_off + 1024 * m, 0, kLoadStream);
             v[2 * m] = u32x2_t{w[0], w[1]};
             v[2 * m + 1] = u32x2_t{w[2], w[3]};
         }
@@ -545,16 +568,21 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     // there would be counted with the tile loads, and waiting for it would
     // wait for every tile still in flight.
     const auto* cplan = readonly_scalar(p.plan);
-    auto plan_at = [&](int i) -> int64_t {
+    // Flat block indices (plan entries, range bounds, cursors) are 32-bit:
+    // every block count fits (checked on the host), and 32-bit compares stay
+    // on the scalar unit, so loop control needs no vector temporaries (a
+    // temporary placed in a register that an in-flight tile load still
+    // targets would make the wave wait for that load).
+    auto plan_at = [&](int i) -> int {
         return __builtin_amdgcn_readfirstlane(LOCAL_PLAN ? plan_sh[i] : cplan[i]);
     };
     const auto* ctable = readonly_scalar(p.table);
     const auto* clens = readonly_scalar(p.kv_lens);
-    const int64_t U = plan_at(p.rows);
+    const int U = plan_at(p.rows);
     const int Q = effective_parts(U, p.parts);
     if (wi >= Q || U <= 0) return;
-    const int64_t u0 = range_start(U, wi, Q);
-    const int64_t u1 = range_start(U, wi + 1, Q);
+    const int u0 = range_start(U, wi, Q);
+    const int u1 = range_start(U, wi + 1, Q);
     if (u0 >= u1) return;
     const bool head_ok = r < p.group;
     const float nan = __builtin_nanf("");
@@ -585,10 +613,28 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     // block 0 and marks its tile bad (the piece's output becomes NaN).
     const int b_first = __builtin_amdgcn_readfirstlane(find_row(LOCAL_PLAN ? plan_sh : p.plan, p.rows, u0));
     int bl = b_first;
-    int64_t lrb0 = plan_at(bl), lrb1 = plan_at(bl + 1);
+    int lrb0 = plan_at(bl), lrb1 = plan_at(bl + 1);
     int l_len = clens[bl];  // kv_len of row bl
-    QReg q, q_next;
-    auto issue = [&](Tile<KV>& t, bool& tbad, int64_t x) {
+    // The query operand of a row lives in one of two LDS slots ([reg][lane],
+    // 16 bytes each): the load cursor fills the next row's slot, the compute
+    // cursor reads its row's slot at every block.  Kept out of loop-carried
+    // registers, a query load is never waited for at the loop's back edge
+    // (a register copy there would also wait for the tile in flight).
+    __shared__ u32x4_t q_sh[2 * kQRegs * 64];
+    auto q_store = [&](int slot, const QReg& v) {
+#pragma unroll
+        for (int i = 0; i < kQRegs; ++i) q_sh[(slot * kQRegs + i) * 64 + lane] = __builtin_bit_cast(u32x4_t, v[i]);
+    };
+    auto q_fetch = [&](int slot, QReg& v) {
+#pragma unroll
+        for (int i = 0; i < kQRegs; ++i)
+            v[i] = __builtin_bit_cast(typename std::remove_reference<decltype(v[0])>::type,
+                                      q_sh[(slot * kQRegs + i) * 64 + lane]);
+    };
+    int lslot = 0;  // slot of the load cursor's row
+    auto issue = [&](Tile<KV>& t, bool& tbad, int x) {
+        bool entered = false;
+        QReg qn;
         if (lrb1 <= x) {
             do {
                 ++bl;
@@ -596,45 +642,54 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
                 lrb1 = plan_at(bl + 1);
             } while (lrb1 <= x);
             l_len = clens[bl];
-            Tile<KV>::load_q(q_next, q_ptr(bl), head_ok, g);
+            Tile<KV>::load_q(qn, q_ptr(bl), head_ok, g);  // requested before the tile, so waited for alone
+            entered = true;
         }
         const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + p.prefix_blocks + (x - lrb0)];
         const bool ok = id >= 0 && id < p.num_blocks;
         tbad = !ok;
         const int64_t off = static_cast<int64_t>(ok ? id : 0) * blk_stride;
         t.load(kpool + off, vpool + off, r, g);
+        if (entered) {
+            lslot ^= 1;
+            q_store(lslot, qn);
+        }
     };
 
     Tile<KV> t[2];
     bool tbad[2];
-    issue(t[0], tbad[0], u0);
-    Tile<KV>::load_q(q, q_ptr(b_first), head_ok, g);
+    {
+        QReg q0;
+        Tile<KV>::load_q(q0, q_ptr(b_first), head_ok, g);
+        issue(t[0], tbad[0], u0);
+        q_store(0, q0);
+    }
+    int cslot = 0;  // slot of the compute cursor's row
 
     // compute cursor: row bc with blocks crb0 .. crb1 - 1; the piece (this
     // wavefront's part of the row) ends at flat block piece_end; tokens at or
     // past t1 are masked
     int bc = b_first;
-    int64_t crb0 = lrb0, crb1 = lrb1;
+    int crb0 = lrb0, crb1 = lrb1;
     int c_len = l_len;
-    int64_t piece_end = u0;  // forces the set-up of the first piece
+    int piece_end = u0;  // forces the set-up of the first piece
     int t1 = 0;
     bool pbad = false;
     Online o;
     // One block x: computed from `cur` while block x + 1 (the range's last
     // block again at its end: a cache hit, never used) loads into `nxt`.  A
-    // new row's query is taken over from q_next before that load, which may
-    // request the query of the row after.
-    auto step = [&](Tile<KV>& cur, bool tb, Tile<KV>& nxt, bool& nb, int64_t x) {
+    // new row takes over the load cursor's query slot before that load, which
+    // may fill the other slot with the query of the row after.
+    auto step = [&](Tile<KV>& cur, bool tb, Tile<KV>& nxt, bool& nb, int x) {
         const bool first = x == piece_end;  // first block of a piece
         if (first && x > u0) {
             // a later row: the load cursor, which loaded block x, is still in
-            // it, with its bounds, length and query
+            // it, with its bounds, length and query slot
             bc = bl;
             crb0 = lrb0;
             crb1 = lrb1;
             c_len = l_len;
-#pragma unroll
-            for (int i = 0; i < kQRegs; ++i) q[i] = q_next[i];
+            cslot = lslot;
         }
         issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
         if (first) {
@@ -651,6 +706,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         }
         pbad = pbad || tb;
         const int tok0 = (p.prefix_blocks + static_cast<int>(x - crb0)) * kBS;
+        QReg q;
+        q_fetch(cslot, q);
         o.step<KV>(cur, q, scale, tok0 + 4 * g, t1, tok0 + kBS);
         if (x + 1 == piece_end) {  // last block of the piece: write it
             float l = o.l;
@@ -676,7 +733,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     };
 
     // two blocks per trip, so the ring slots are fixed registers
-    for (int64_t x = u0; x < u1; x += 2) {
+    for (int x = u0; x < u1; x += 2) {
         step(t[0], tbad[0], t[1], tbad[1], x);
         if (x + 1 >= u1) break;
         step(t[1], tbad[1], t[0], tbad[0], x + 1);
