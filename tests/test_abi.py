@@ -248,3 +248,30 @@ def test_error_codes():
     pk.seq_append(p, t, 30)
     with pytest.raises(pk.PagedKVError):
         pk.block_table_build(p, [t], 1)
+
+
+def test_attention_rejects_block_counts_beyond_32_bits():
+    """The kernels sum block counts over rows in 32 bits: rows x
+    ceil(max_kv_len / 16) at or above 2^31 is rejected before any launch
+    (the workspace query runs the same checks and touches no device memory)."""
+    import ctypes
+
+    c = pk.pkv_cache()
+    c.kv_dtype, c.num_layers, c.num_blocks, c.num_kv_heads = 1, 1, 1024, 8
+    c.head_dim, c.block_size = 128, 16
+    c.k_pool = c.v_pool = 1 << 20  # never dereferenced by the checks
+    n = ctypes.c_size_t(0)
+
+    def size(num_seqs, max_kv_len):
+        a = pk.pkv_attn_args()
+        a.layer, a.q_dtype, a.num_seqs, a.num_q_heads = 0, 1, num_seqs, 32
+        a.q = a.out = a.block_table = a.kv_lens = 1 << 20
+        a.max_kv_len = max_kv_len
+        a.max_blocks = (max_kv_len + 15) // 16
+        return pk._lib.paged_attn_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n))
+
+    assert size(64, 8192) == 0 and n.value > 0
+    # 2^31 / 2^15 = 65536 rows of 2^19 tokens (2^15 blocks) is the first count that does not fit
+    assert size(65535, 1 << 19) == 0
+    assert size(65536, 1 << 19) == -1
+    assert "2^31" in pk._lib.pkv_last_error().decode()
