@@ -226,6 +226,37 @@ def test_invalid_rows_give_nan_and_others_stay_right():
     del good
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_runs_of_short_rows(kv):
+    """Rows of one to three blocks in a run: a wavefront enters a new row at
+    nearly every block, so each row's query must reach the compute side in
+    order (it is handed over through a slot per row) while the next row's
+    query is already being fetched.  One wavefront per kv head walks every
+    row; other partitions cut the run in different places.  Empty rows in
+    the run (length 0) get NaN and are skipped without disturbing the
+    hand-over of their neighbours."""
+    import paged_kv_cache_263_amd as pk
+
+    rng = np.random.default_rng(71)
+    lens = [int(x) for x in rng.integers(1, 49, size=96)]
+    hq, hkv = (8, 2) if kv == "f32" else (16, 2)
+    w = W.custom(lens, hq, hkv, kv, seed=73, variant="peaked")
+    for parts in (1, 3, 0):
+        check_decode(w, decode_parts=parts)
+    hip = HipSide(w)
+    lens_dev = hip.kv_lens.clone()
+    empty = [5, 6, 40, 95]
+    lens_dev[empty] = 0
+    case(f"short rows {kv} with empty rows {empty}")
+    out = pk.paged_attn_decode(hip.cache, hip.q, hip.table, lens_dev, hip.max_kv_len, decode_parts=1)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[empty].float()).all()
+    orc = OracleSide(w)
+    keep = [b for b in range(len(lens)) if b not in empty]
+    ref = np.stack([orc.decode(b) for b in keep])
+    compare(out[keep].float().cpu().numpy(), ref, TOL[w.kv_dtype], f"short rows {kv} around empty rows")
+
+
 @pytest.mark.parametrize("rows", [1024, 1100])
 def test_many_rows_both_plan_paths(rows):
     """Up to 1024 rows, every decode wavefront computes the prefix sum of
