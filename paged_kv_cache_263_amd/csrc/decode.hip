@@ -430,6 +430,42 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
 // row's first piece waits for a few memory round trips, not two per range.
 constexpr int kMaxPrefixParts = 8;
 
+// The states of up to two key ranges, requested in one round before the
+// next tile's loads so that waiting for them waits for nothing else.
+struct PrefixLoads {
+    f32x4_t a0[8], a1[8];
+    float2 ml0, ml1;
+};
+__device__ __forceinline__ void prefix_request(const DecodeParams& p, int64_t qrow, int g, PrefixLoads& pl) {
+    const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
+    const float* s0 = p.ws_prefix + qrow * kPrefixState;
+    const float* s1 = p.prefix_parts > 1 ? s0 + stride : s0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) pl.a0[n] = ld<f32x4_t>(s0 + 16 * n + 4 * g);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) pl.a1[n] = ld<f32x4_t>(s1 + 16 * n + 4 * g);
+    pl.ml0 = ld<float2>(s0 + kD);
+    pl.ml1 = ld<float2>(s1 + kD);
+}
+// The same combination as prefix_state, in the same order, from loaded states.
+__device__ __forceinline__ float prefix_combine(const DecodeParams& p, int g, const PrefixLoads& pl, f32x4_t acc[8],
+                                                float& l) {
+    const bool two = p.prefix_parts > 1;
+    const float mx = two ? fmaxf(pl.ml0.x, pl.ml1.x) : pl.ml0.x;
+    const float w0 = __builtin_amdgcn_exp2f(pl.ml0.x - mx);
+    float lsum = pl.ml0.y * w0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = pl.a0[n] * w0;
+    if (two) {
+        const float w1 = __builtin_amdgcn_exp2f(pl.ml1.x - mx);
+        lsum += pl.ml1.y * w1;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] += pl.a1[n] * w1;
+    }
+    l = g == 0 ? lsum : 0.f;
+    return mx;
+}
+
 __device__ __forceinline__ float prefix_state(const DecodeParams& p, int64_t qrow, int g, f32x4_t acc[8], float& l) {
     const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
     const float* ps = p.ws_prefix + qrow * kPrefixState;
@@ -691,18 +727,21 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
             c_len = l_len;
             cslot = lslot;
         }
+        // the row's first piece starts from its state over the shared prefix,
+        // the states of the prefix's key ranges combined (one lane group
+        // carries the normaliser); up to two ranges are requested before the
+        // next tile
+        const bool pstart = p.prefix_blocks > 0 && first && x == crb0;
+        const bool pfew = p.prefix_parts <= 2;
+        PrefixLoads pl;
+        if (pstart && pfew) prefix_request(p, qrow_of(bc), g, pl);
         issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
         if (first) {
             piece_end = crb1 < u1 ? crb1 : u1;
             t1 = min(c_len, (p.prefix_blocks + static_cast<int>(piece_end - crb0)) * kBS);
             pbad = false;
             o = Online();
-            if (p.prefix_blocks > 0 && x == crb0) {
-                // the row's first piece starts from its state over the shared
-                // prefix, the states of the prefix's key ranges combined (one
-                // lane group carries the normaliser)
-                o.m = prefix_state(p, qrow_of(bc), g, o.acc, o.l);
-            }
+            if (pstart) o.m = pfew ? prefix_combine(p, g, pl, o.acc, o.l) : prefix_state(p, qrow_of(bc), g, o.acc, o.l);
         }
         pbad = pbad || tb;
         const int tok0 = (p.prefix_blocks + static_cast<int>(x - crb0)) * kBS;
