@@ -89,11 +89,27 @@ constexpr int kPrefixState = kD + 4;
 // cover all 64 banks.
 __device__ __forceinline__ int v_lds_offset(int d, int h) { return d * kBS + 8 * (h ^ ((d >> 3) & 1)); }
 
+// bf16 V piece staged by thread t: a permutation of the pieces inside each
+// wave's contiguous 1 KiB of the tile (so the global load stays one
+// contiguous run per wave), chosen so that every 16 lanes of the two 8-byte
+// LDS stores below write distinct banks.  Lane 16 a + b takes d row
+// r = 4 a + b % 4 (and r + 16) of the wave's 32 rows, token group
+// g = 2 h + (b / 4) % 2 with h = (b / 8) ^ (a / 2).
+struct VPiece {
+    int r, g;
+};
+__device__ __forceinline__ VPiece v_piece(int t) {
+    const int a = (t >> 4) & 3, b = t & 15;
+    const int r = 4 * a + (b & 3);
+    const int h = ((b >> 3) & 1) ^ (a >> 1);
+    return VPiece{r, 2 * h + ((b >> 2) & 1)};
+}
+
 // Staging registers for one iteration: thread t owns 16 bytes of each of the
-// iteration's 4 K tiles and 4 V tiles.  bf16 tiles: piece t of the tile
-// (bf16_k_offset, bf16_v_offset), so 256 threads read each 4 KiB tile
-// contiguously; K piece t is token t%16, d 8(t/16)..+7, and V piece t holds
-// tokens 4g..4g+3 (g = (t/16)%4) of d rows 32(t/64) + t%16 and that + 16.
+// iteration's 4 K tiles and 4 V tiles.  bf16 tiles (bf16_k_offset,
+// bf16_v_offset): K piece t, token t%16, d 8(t/16)..+7; V piece
+// 64 (t/64) + 16 g + r (v_piece), tokens 4g..4g+3 of d rows 32(t/64) + r and
+// that + 16; 256 threads read each 4 KiB tile contiguously.
 // One-byte tiles: K row t/16, elements (t%16)*8..+7, and V d row t/2, tokens
 // (t%2)*8..+7, their codes converted to bf16 on load.
 // The tile addresses are uniform (one per block) and the thread's offset
@@ -130,7 +146,7 @@ struct Stage {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // token of element e
-                const int tok = KV == PKV_BF16 ? 4 * ((t >> 4) & 3) + (e & 3) : (t & 1) * 8 + e;
+                const int tok = KV == PKV_BF16 ? 4 * v_piece(t).g + (e & 3) : (t & 1) * 8 + e;
                 if (tok >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
             }
             v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
@@ -141,8 +157,9 @@ struct Stage {
         for (int b = 0; b < 4; ++b) {
             if constexpr (KV == PKV_BF16) {
                 st<u32x4_t>(ks + (b * kBS + (t & 15)) * kKStride + 8 * (t >> 4), k[b]);
-                const int g = (t >> 4) & 3;
-                const int d0 = 32 * (t >> 6) + (t & 15);
+                const VPiece vp = v_piece(t);
+                const int g = vp.g;
+                const int d0 = 32 * (t >> 6) + vp.r;
                 uint16_t* vt = vs + b * kTile + 4 * (g & 1);
                 st<u32x2_t>(vt + v_lds_offset(d0, g >> 1), u32x2_t{v[b][0], v[b][1]});
                 st<u32x2_t>(vt + v_lds_offset(d0 + 16, g >> 1), u32x2_t{v[b][2], v[b][3]});
@@ -241,7 +258,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const uint32_t koff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : ((t >> 4) * kD + (t & 15) * 8) * kElt);
-    const uint32_t voff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : byte_v_offset(t >> 1, (t & 1) * 8));
+    const uint32_t voff = static_cast<uint32_t>(
+        KV == PKV_BF16 ? 16 * (64 * (t >> 6) + 16 * v_piece(t).g + v_piece(t).r) : byte_v_offset(t >> 1, (t & 1) * 8));
     const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(t >> 1, (t & 1) * 8 + 4));
     // LDS element offsets of this lane's operands
     const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
