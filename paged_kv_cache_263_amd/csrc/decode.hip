@@ -580,7 +580,13 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
     __syncthreads();
 }
 
-template <int KV, bool LOCAL_PLAN>
+// QMEM: the query operand is read from memory at every block (the row's
+// query rows stay in the caches) instead of from its LDS slot.  Chosen for
+// bf16 caches with at most four query heads per kv head, where it measured
+// faster (Llama-shaped batch, 4 heads: 183 against 189 us); with eight heads
+// the extra reads cost more than they save (shared-prefix batch: 161 against
+// 155 us), and one-byte tiles are smaller still, so those keep the slots.
+template <int KV, bool LOCAL_PLAN, bool QMEM>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
                 lrb1 = plan_at(bl + 1);
             } while (lrb1 <= x);
             l_len = clens[bl];
-            Tile<KV>::load_q(qn, q_ptr(bl), head_ok, g);  // requested before the tile, so waited for alone
+            if constexpr (!QMEM) Tile<KV>::load_q(qn, q_ptr(bl), head_ok, g);  // requested before the tile, so waited for alone
             entered = true;
         }
         const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + p.prefix_blocks + (x - lrb0)];
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         tbad = !ok;
         const int64_t off = static_cast<int64_t>(ok ? id : 0) * blk_stride;
         t.load(kpool + off, vpool + off, r, g);
-        if (entered) {
+        if (entered && !QMEM) {
             lslot ^= 1;
             q_store(lslot, qn);
         }
@@ -694,7 +700,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
     Tile<KV> t[2];
     bool tbad[2];
-    {
+    if constexpr (QMEM) {
+        issue(t[0], tbad[0], u0);
+    } else {
         QReg q0;
         Tile<KV>::load_q(q0, q_ptr(b_first), head_ok, g);
         issue(t[0], tbad[0], u0);
@@ -735,6 +743,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         const bool pfew = p.prefix_parts <= 2;
         PrefixLoads pl;
         if (pstart && pfew) prefix_request(p, qrow_of(bc), g, pl);
+        QReg qm;
+        if constexpr (QMEM) Tile<KV>::load_q(qm, q_ptr(bc), head_ok, g);
         issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
         if (first) {
             piece_end = crb1 < u1 ? crb1 : u1;
@@ -746,7 +756,12 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         pbad = pbad || tb;
         const int tok0 = (p.prefix_blocks + static_cast<int>(x - crb0)) * kBS;
         QReg q;
-        q_fetch(cslot, q);
+        if constexpr (QMEM) {
+#pragma unroll
+            for (int i = 0; i < kQRegs; ++i) q[i] = qm[i];
+        } else {
+            q_fetch(cslot, q);
+        }
         o.step<KV>(cur, q, scale, tok0 + 4 * g, t1, tok0 + kBS);
         if (x + 1 == piece_end) {  // last block of the piece: write it
             float l = o.l;
@@ -945,16 +960,19 @@ template <bool LOCAL>
 void launch_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const DecodeParams& p) {
     switch (kv_dtype) {
         case PKV_F32:
-            hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
-            hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL>), grid, dim3(64), 0, stream, p);
+            if (p.group <= 4)
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true>), grid, dim3(64), 0, stream, p);
+            else
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_FP8_E4M3:
-            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
     }
 }
