@@ -379,6 +379,23 @@ def test_shared_prefix_pass(kv, variant):
     assert (out.float() - plain.float()).abs().max().item() <= 2 * TOL[w.kv_dtype]
 
 
+@pytest.mark.parametrize("variant", ["peaked", "needle"])
+def test_shared_prefix_pass_four_heads_per_kv_head(variant):
+    """The shared-prefix promise with four query heads per kv head (a bf16
+    cache then reads each block's query operand from memory rather than from
+    its LDS slot): matches the oracle, agrees with the plain decode within
+    tolerance, and is deterministic."""
+    w = W.shared_prefix(nseq=48, max_suffix=300, hq=32, hkv=8, variant=variant)
+    hip = HipSide(w)
+    rows = [0, 1, 2, 23, 46, 47]
+    _, out = check_decode(w, rows=rows, hip=hip, shared_prefix_blocks=125)
+    plain = hip.decode()
+    again = hip.decode(shared_prefix_blocks=125)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    assert (out.float() - plain.float()).abs().max().item() <= 2 * TOL[w.kv_dtype]
+
+
 def test_shared_prefix_pass_rows_without_suffix():
     """Rows that end exactly at the shared prefix take their output from the
     prefix state alone; a row shorter than the prefix is invalid (NaN)."""
