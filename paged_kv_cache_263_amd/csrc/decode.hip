@@ -20,10 +20,12 @@
 // and head (i % 16) of the B operand and of the result, so scores, softmax
 // state and output of head i % 16 stay in the lanes that own that head: the
 // only cross-lane traffic is the max and sum over the four 16-lane groups
-// (two xor shuffles, only when the running maximum moves).  With K stored
-// [tok][d] and V stored [d][tok] inside a block, every lane's operand is one
-// contiguous 16 / 8 / 4-byte load and a wave reads each 4 KiB (bf16) tile in
-// whole cache lines.  P is split into a bf16 high part and a bf16 remainder,
+// (two xor shuffles, only when the running maximum moves).  Inside a block K
+// is token-major and V d-major, with the 16-byte pieces of bf16 and one-byte
+// tiles ordered so that each lane's operands are whole 16-byte loads and each
+// load instruction of a wave reads contiguous runs of the tile
+// (bf16_k_offset, bf16_v_offset, byte_v_offset); fp32 tiles keep the plain
+// [tok][d] and [d][tok] orders.  P is split into a bf16 high part and a bf16 remainder,
 // so P.V keeps ~16 mantissa bits.  fp32 caches use the fp32 matrix
 // instruction (16x16x4) with the same lanes; one-byte caches (fp8 E4M3 and
 // int8) convert their codes to bf16 in registers (exact) and fold the
