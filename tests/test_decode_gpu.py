@@ -136,6 +136,35 @@ def test_one_byte_codes_bit_exact(kv):
         assert (codes != -128).all() and (np.abs(codes) == 127).any()
 
 
+def test_bf16_tile_order_matches_the_header():
+    """The cache write puts bf16 K (token, d) at element
+    (d // 8) * 128 + token * 8 + d % 8 and V (d, token) at element
+    (d // 32) * 512 + ((token // 4) * 16 + d % 16) * 8 + ((d // 16) % 2) * 4 + token % 4
+    of the (block, kv head) tile, bit for bit, at every written position."""
+    w = W.custom([37, 300, 1000], 8, 2, "bf16", seed=33)
+    case("bf16 tile order")
+    hip = HipSide(w)
+    lens, starts = W.replay_lengths(w)
+    kp = hip.cache.k_pool[0].cpu().view(torch.int16).numpy().reshape(w.num_blocks, w.hkv, 2048)
+    vp = hip.cache.v_pool[0].cpu().view(torch.int16).numpy().reshape(w.num_blocks, w.hkv, 2048)
+    dd = np.arange(128)
+    for op in w.script:
+        if op.kind != "append":
+            continue
+        k, v = W.append_values(w, op, "cuda", starts[op.op_id], lens[op.seq])
+        row = hip.table_host[op.seq].numpy()
+        t = np.arange(op.n)
+        blk, off = row[t // 16], t % 16
+        kidx = (dd[None, :] // 8) * 128 + off[:, None] * 8 + dd[None, :] % 8
+        vidx = ((dd[None, :] // 32) * 512 + ((off[:, None] // 4) * 16 + dd[None, :] % 16) * 8
+                + ((dd[None, :] // 16) % 2) * 4 + off[:, None] % 4)
+        for j in range(w.hkv):
+            want_k = k[:, j].cpu().view(torch.int16).numpy()
+            want_v = v[:, j].cpu().view(torch.int16).numpy()
+            assert np.array_equal(kp[blk[:, None], j, kidx], want_k)
+            assert np.array_equal(vp[blk[:, None], j, vidx], want_v)
+
+
 def test_partitions_agree_and_are_deterministic():
     """Any number of wavefronts per kv head (1: one wavefront per head walks
     every row; many: rows cut into pieces and merged) gives the oracle's
