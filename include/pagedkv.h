@@ -146,8 +146,9 @@ int seq_len(const pkv_pool* pool, int32_t seq, int32_t* out_len);
 int seq_num_blocks(const pkv_pool* pool, int32_t seq, int32_t* out_n);
 
 /* Swapping a sequence to host memory when blocks run out ([P2] "When it runs
- * out anyway": ship the blocks over PCIe and bring them back; [P3] "M.65
- * Inference Serving": overflow blocks to CPU memory, reload them).
+ * out anyway": a preempted request's blocks move across the host link to CPU
+ * memory and come back later; [P3] "M.65 Inference Serving": the same
+ * spill-and-reload of blocks).
  * seq_swap_out: out_ids host [cap] receives seq's block ids in logical order
  * (*n_out = ceil(len / 16)); then one reference is dropped from each, in that
  * order, and seq is swapped out: it keeps its length and holds no blocks.
@@ -255,7 +256,8 @@ typedef struct {
     const int32_t* cu_q;         /* device [num_seqs + 1]: row i's queries are cu_q[i]..cu_q[i+1]-1 */
     int32_t num_decode;          /* rows 0..num_decode-1 have exactly one query (cu_q[i] = i) */
     int32_t max_decode_kv_len;   /* host: bound on the decode rows' kv_lens (0 = max_kv_len) */
-    int32_t max_q_len;           /* host: upper bound on the other rows' query counts */
+    int32_t max_q_len;           /* host: upper bound on the other rows' query counts (a chunk row
+                                    with more queries is invalid: all its outputs are NaN) */
     int32_t total_q;             /* host: cu_q[num_seqs] */
     /* tuning and scratch: */
     int32_t decode_parts;        /* decode: the blocks of each kv head are divided evenly among this
@@ -267,7 +269,10 @@ typedef struct {
                                     same block ids (a prefix all rows share); the call then computes
                                     attention over those blocks once for all rows and continues each
                                     row from there.  Each row's kv_lens must be at least 16 times
-                                    this (else the row is invalid).  0 = no promise. */
+                                    this (else the row is invalid).  The promise is checked on the
+                                    device: a row whose first shared_prefix_blocks ids differ from
+                                    row 0's gets NaN output, the other rows are unaffected.
+                                    0 = no promise. */
     void* workspace;             /* device scratch: row plan and partial results */
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
@@ -310,7 +315,10 @@ int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* s
  * cached tokens (their K/V already written), and query j attends keys
  * 0..kv_lens[i]-C_i+j (causal, bottom-right aligned).  Chunk rows need a
  * bf16, fp8 or int8 cache (PKV_ERR_UNSUPPORTED for fp32).  A chunk row with an
- * invalid length or block id gets NaN output. */
+ * invalid length or block id, or with more queries than max_q_len, gets NaN
+ * output.  The kernels trust cu_q to be non-decreasing and within
+ * 0..total_q: a row whose cu_q entries are not is left unwritten (its output
+ * place is unknown). */
 int paged_attn_prefill_chunk(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
 /* Write n_tokens new tokens' K and V into the cache at their slots (fp8:

@@ -45,9 +45,9 @@ library follows the same documented policy independently):
   [P3] item (g)); ``share_prefix`` shares the first n tokens, n a multiple of
   16 (prefix matching is block aligned, [P2] "Fast answers").
 * ``free`` drops one reference to each block of the sequence, in logical order.
-* Swapping to host memory ([P2] "When it runs out anyway": ship the blocks over
-  PCIe and bring them back; [P3] "M.65 Inference Serving": overflow blocks to
-  CPU memory and reload them).  ``swap_out`` returns the sequence's block ids
+* Swapping to host memory ([P2] "When it runs out anyway": a preempted
+  request's blocks move across the host link to CPU memory and return later;
+  [P3] "M.65 Inference Serving": the same spill-and-reload of blocks).  ``swap_out`` returns the sequence's block ids
   in logical order (the caller copies those blocks to host memory before any
   of them is reused) and drops one reference to each, in that order; the
   sequence keeps its length and holds no blocks while swapped.  ``swap_in``

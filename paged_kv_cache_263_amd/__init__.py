@@ -410,6 +410,16 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _torch_stream(stream, device):
+    """The torch stream object a call's kernels are enqueued on (the current
+    stream, the given one, or a raw hipStream_t handle wrapped)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -482,14 +492,24 @@ def paged_attn_workspace_size(cache: KVCache, args: pkv_attn_args) -> int:
     return n.value
 
 
-def _with_workspace(cache, a, workspace, device):
+def _with_workspace(cache, a, workspace, device, ts):
+    """Workspace for the call: the caller's, or one allocated here under the
+    call's own stream ``ts``, so that the caching allocator hands its memory
+    to nothing else before the kernels on ``ts`` that use it have run."""
     if workspace is None:
         need = paged_attn_workspace_size(cache, a)
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+            with torch.cuda.stream(ts):
+                workspace = torch.empty(need, dtype=torch.uint8, device=device)
             a.workspace = workspace.data_ptr()
             a.workspace_bytes = need
     return workspace
+
+
+def _new_out(q, ts):
+    # allocated on the call's stream for the same reason as the workspace
+    with torch.cuda.stream(ts):
+        return torch.empty_like(q)
 
 
 def _set_events(a, events):
@@ -505,13 +525,14 @@ def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, 
     four hipEvent_t handles (ints) recorded around the kernels (see the header).
     ``shared_prefix_blocks``: the caller's promise that every row's table starts
     with the same that many block ids (attention over them is computed once)."""
+    ts = _torch_stream(stream, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(q, ts)
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace)
     a.shared_prefix_blocks = shared_prefix_blocks
     _set_events(a, events)
-    keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841 (alive until enqueued)
-    _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
+    keep = _with_workspace(cache, a, workspace, q.device, ts)  # noqa: F841 (stream-ordered reuse)
+    _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(ts)))
     return out
 
 
@@ -519,14 +540,15 @@ def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_
                              max_q_len: int, out=None, layer: int = 0, max_decode_kv_len: int = 0,
                              decode_parts: int = 0, workspace=None, stream=None, events=None):
     """q [total_q, Hq, 128]; rows 0..num_decode-1 are decode rows (cu_q[i] = i)."""
+    ts = _torch_stream(stream, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = _new_out(q, ts)
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace, cu_q=cu_q,
               num_decode=num_decode, max_decode_kv_len=max_decode_kv_len, max_q_len=max_q_len,
               total_q=q.shape[0])
     _set_events(a, events)
-    keep = _with_workspace(cache, a, workspace, q.device)  # noqa: F841
-    _check(_lib.paged_attn_prefill_chunk(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
+    keep = _with_workspace(cache, a, workspace, q.device, ts)  # noqa: F841 (stream-ordered reuse)
+    _check(_lib.paged_attn_prefill_chunk(ctypes.byref(cache.desc), ctypes.byref(a), _stream(ts)))
     return out
 
 

@@ -67,7 +67,7 @@ struct PrefillParams {
     const int32_t* table;   // [num_seqs][max_blocks]
     const int32_t* kv_lens; // [num_seqs]
     const int32_t* cu_q;    // [num_seqs + 1]
-    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, q_tiles, total_q, tile_tokens;
+    int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, max_q_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
     // shared-prefix pass (PREFIX kernels): the decode rows' queries (one per
     // row, total_q rows) over the first prefix_tokens keys of table row 0, no
@@ -208,7 +208,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     if (j0 >= C || qbeg < 0 || qbeg + C > p.total_q) return;  // (a malformed cu_q writes nothing)
     // P: keys before the chunk (prefix pass: the prefix; every query sees all of it)
     const int L = PREFIX ? p.prefix_tokens : p.kv_lens[row];
-    const bool row_ok = PREFIX ? L >= kBS : C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS;
+    // a chunk row with more queries than max_q_len is invalid: every query of
+    // it gets NaN, the last tile filling the queries that no tile owns
+    const int covered = p.q_tiles * p.tile_tokens;
+    const bool over = !PREFIX && C > p.max_q_len;
+    const bool row_ok = PREFIX ? L >= kBS
+                               : C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS && !over;
+    if (!PREFIX && C > covered && qt == p.q_tiles - 1) {
+        const u32x4_t nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};  // bf16 NaN x 8
+        const int pieces = (C - covered) * p.group * (kD / 8);
+        for (int e = t; e < pieces; e += 256) {
+            const int tok_e = covered + e / (p.group * (kD / 8));
+            const int rest = e % (p.group * (kD / 8));
+            uint16_t* o = static_cast<uint16_t*>(p.out) +
+                          (static_cast<int64_t>(qbeg + tok_e) * p.hq + kvh * p.group + rest / (kD / 8)) * kD +
+                          8 * (rest % (kD / 8));
+            st<u32x4_t>(o, nan8);
+        }
+    }
+    // Prefix pass: the caller promises that every row's table starts with
+    // row 0's first prefix_tokens / 16 block ids.  Each workgroup checks the
+    // promise for its own rows; a row that breaks it gets a NaN state, so its
+    // output is NaN like that of any other invalid row.
+    __shared__ int broken[kRows];
+    if constexpr (PREFIX) {
+        for (int i = t; i < p.tile_tokens; i += 256) broken[i] = 0;
+        __syncthreads();
+        const int S = p.prefix_tokens / kBS;
+        const int ntok = min(p.tile_tokens, C - j0);
+        for (int e = t; e < ntok * S; e += 256) {
+            const int r = e / S, b = e - r * S;
+            if (p.table[static_cast<int64_t>(j0 + r) * p.max_blocks + b] != p.table[b]) broken[r] = 1;
+        }
+        // (read after the barrier that follows the first stage store)
+    }
     const int P = PREFIX ? L : L - C;
     const int jmax = min(j0 + p.tile_tokens, C);  // exclusive
     const int kend = row_ok ? (PREFIX ? P : P + jmax) : 0;  // keys this tile needs
@@ -397,6 +430,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     }
 
     bad = bad || !row_ok;
+    if constexpr (PREFIX) bad = bad || (qrow_ok && broken[tok] != 0);
     l += __shfl_xor(l, 32);
     if (!qrow_ok) return;
     if constexpr (PREFIX) {  // the state, unnormalised (the decode kernel continues from it)
@@ -538,6 +572,7 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.group = group;
     p.max_blocks = a->max_blocks;
     p.max_kv_len = a->max_kv_len;
+    p.max_q_len = a->max_q_len;
     p.q_tiles = q_tiles;
     p.total_q = a->total_q;
     p.tile_tokens = tile_tokens;

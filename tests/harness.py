@@ -135,9 +135,10 @@ class OracleSide:
                                                 self.final_lens[op.seq])
         return self._vals[op_id]
 
-    def row_kv(self, row: int, kvh: int, upto: int | None = None):
+    def row_kv(self, row: int, kvh: int, upto: int | None = None, quantised: bool = True):
         """float64 K, V [L, d] of one row and kv head, read through the oracle's
-        table (and, for fp8, through the oracle's quantiser)."""
+        table (and, for fp8 and int8, through the oracle's quantiser unless
+        ``quantised`` is False: then the values before storage)."""
         seq = self.w.batch[row]
         L = self.pool.seq_len(seq) if upto is None else upto
         ids = self.store.gather(self.pool.seq_blocks(seq), L)
@@ -151,22 +152,23 @@ class OracleSide:
             kk = k[idx, kvh].float().cpu().numpy()
             vv = v[idx, kvh].float().cpu().numpy()
             codec = {"fp8": OF, "int8": OI}.get(self.w.kv_dtype)
-            if codec is not None:
+            if codec is not None and quantised:
                 kk = codec.dequantise(codec.quantise_scaled(kk, self.w.k_scale[kvh]), self.w.k_scale[kvh])
                 vv = codec.dequantise(codec.quantise_scaled(vv, self.w.v_scale[kvh]), self.w.v_scale[kvh])
             K[sel] = kk
             V[sel] = vv
         return K, V
 
-    def decode(self, row: int, heads=None) -> np.ndarray:
-        """Oracle output [len(heads), d] for a decode row."""
+    def decode(self, row: int, heads=None, quantised: bool = True) -> np.ndarray:
+        """Oracle output [len(heads), d] for a decode row (over the values
+        before fp8 / int8 storage if ``quantised`` is False)."""
         w = self.w
         heads = list(range(w.hq)) if heads is None else list(heads)
         q = W.query_row(w, row, self.device)[0].float().cpu().numpy()
         out = np.empty((len(heads), w.d))
         for j in sorted({h // w.group for h in heads}):
             hs = [h for h in heads if h // w.group == j]
-            K, V = self.row_kv(row, j)
+            K, V = self.row_kv(row, j, quantised=quantised)
             o = OA.decode_rows(q[hs], K[:, None, :], V[:, None, :], list(range(len(hs))))
             for h, oo in zip(hs, o):
                 out[heads.index(h)] = oo

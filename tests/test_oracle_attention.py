@@ -142,3 +142,37 @@ def test_prefill_rows_are_chunk_rows():
     full = A.prefill_chunk(q, K, V)
     rows = [0, 5, 11]
     np.testing.assert_allclose(A.prefill_rows(q, K, V, rows), full[rows], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("hq,hkv,L,scale", [(8, 2, 37, 1.0), (4, 4, 5, 4.0), (8, 1, 70, 4.0), (32, 8, 129, 1.0),
+                                            (12, 2, 50, 4.0), (6, 3, 17, 2.0)])
+def test_decode_rows_matches_sdpa_and_decode(hq, hkv, L, scale):
+    """decode_rows (the sampled-head form every GPU decode comparison uses)
+    gives the listed heads of torch SDPA's grouped-query attention and of
+    decode, for head lists in any order, with repeats, across every kv head."""
+    d = 128 if hq != 32 else 64
+    q = rnd((hq, d), 41, scale)
+    K, V = rnd((L, hkv, d), 42), rnd((L, hkv, d), 43)
+    ref = sdpa(q[None], K, V)[0]
+    full = A.decode(q, K, V)
+    rng = np.random.default_rng(44)
+    for heads in (list(range(hq)), list(range(hq))[::-1], rng.integers(0, hq, 7).tolist(), [hq - 1, 0, hq - 1]):
+        got = A.decode_rows(q, K, V, heads)
+        assert got.shape == (len(heads), d)
+        np.testing.assert_allclose(got, ref[heads], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(got, full[heads], rtol=0, atol=1e-13)
+
+
+def test_decode_rows_kv_head_of_each_query_head():
+    """Each query head reads kv head h // G: with V constant per kv head
+    (value j + 1 for kv head j), head h's output is exactly h // G + 1."""
+    hq, hkv, d, L = 12, 3, 16, 9
+    q = rnd((hq, d), 45, 3.0)
+    K = rnd((L, hkv, d), 46)
+    V = np.empty((L, hkv, d))
+    for j in range(hkv):
+        V[:, j, :] = j + 1.0
+    heads = [11, 0, 4, 7, 8, 3]
+    got = A.decode_rows(q, K, V, heads)
+    for n, h in enumerate(heads):
+        np.testing.assert_allclose(got[n], h // (hq // hkv) + 1.0, rtol=0, atol=1e-14)
