@@ -308,6 +308,20 @@ int paged_attn_workspace_size(const pkv_cache* cache, const pkv_attn_args* args,
  * order); it is still independent of where the blocks sit. */
 int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
+/* paged_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid hipMalloc):
+ * the same kernels and result, with the workspace taken from a fixed array of
+ * PKV_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends.  args->workspace must be NULL and
+ * workspace_bytes 0.  A call whose paged_attn_workspace_size exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES is PKV_ERR_WORKSPACE (nothing launched).  The
+ * call allocates nothing.  stream must belong to the current device.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams with no ordering between them) race; calls on one stream
+ * are safe. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_attn_decode_noalloc(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
+
 /* Chunked prefill batched with decode rows ([P1] "Serving systems: the layer
  * that survives real traffic"; [P3] "prefill vs decode phase separation",
  * item (e)).  Rows 0..num_decode-1 are decode rows; each other row i holds

@@ -23,7 +23,7 @@ __all__ = [
     "seq_create", "seq_append", "seq_append_batch", "seq_fork", "seq_share_prefix", "seq_free",
     "seq_len", "seq_num_blocks", "seq_swap_out", "seq_swap_in", "seq_create_cached", "seq_cache_tokens",
     "block_table_build",
-    "paged_attn_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
+    "paged_attn_workspace_size", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_prefill_chunk",
     "kv_cache_write", "kv_copy_blocks", "kv_swap_block_bytes", "kv_swap_out", "kv_swap_in",
     "pkv_strerror", "pkv_last_error", "pkv_version",
 ]
@@ -106,6 +106,7 @@ _SIGNATURES = {
     "paged_attn_workspace_size": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args),
                                                  ctypes.POINTER(ctypes.c_size_t)]),
     "paged_attn_decode": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args), _p]),
+    "paged_attn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args), _p]),
     "paged_attn_prefill_chunk": (ctypes.c_int, [ctypes.POINTER(pkv_cache), ctypes.POINTER(pkv_attn_args), _p]),
     "kv_cache_write": (ctypes.c_int, [ctypes.POINTER(pkv_cache), _i32, _i32, _i32, _p, _p, _p, _p, _p, _i32,
                                       _p, _i32, _p, _p]),
@@ -533,6 +534,23 @@ def paged_attn_decode(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, 
     _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device, ts)  # noqa: F841 (stream-ordered reuse)
     _check(_lib.paged_attn_decode(ctypes.byref(cache.desc), ctypes.byref(a), _stream(ts)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attn_decode_noalloc(cache: KVCache, q, block_table, kv_lens, max_kv_len: int, out, layer: int = 0,
+                              decode_parts: int = 0, stream=None, events=None, shared_prefix_blocks: int = 0):
+    """paged_attn_decode with no allocation anywhere (nor here): ``out`` is the
+    caller's, and the workspace is the library's fixed per-GPU array of
+    NOALLOC_SCRATCH_BYTES (calls that overlap on one GPU race on it)."""
+    if out is None:
+        raise PagedKVError(-1, "paged_attn_decode_noalloc needs the caller's out tensor")
+    a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, None)
+    a.shared_prefix_blocks = shared_prefix_blocks
+    _set_events(a, events)
+    _check(_lib.paged_attn_decode_noalloc(ctypes.byref(cache.desc), ctypes.byref(a), _stream(stream)))
     return out
 
 

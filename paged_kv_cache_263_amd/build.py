@@ -26,7 +26,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 
-SOURCES = ["errors.cpp", "checks.cpp", "pool.cpp", "decode.hip", "prefill.hip", "cache_ops.hip"]
+SOURCES = ["errors.cpp", "checks.cpp", "pool.cpp", "decode.hip", "prefill.hip", "cache_ops.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
