@@ -28,7 +28,9 @@ __all__ = [
     "pkv_strerror", "pkv_last_error", "pkv_version",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PKV_LIBRARY names another build of the same library (the sanitized host
+# build that tests the allocator under ASan/UBSan); by default the in-tree one.
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PKV_F32, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3
 BLOCK_SIZE = 16
