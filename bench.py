@@ -100,6 +100,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=WORKLOADS)
     ap.add_argument("--decode-parts", type=int, default=0, help="wavefronts per kv head (0 = auto)")
     ap.add_argument("--context", type=int, default=16384, help="chunked: cached context before the chunk")
+    ap.add_argument("--chunk", type=int, default=1024, help="chunked: queries in the chunk")
+    ap.add_argument("--prefill-parts", type=int, default=0, help="chunked: key ranges per query tile (0 = auto)")
     ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8", "int8"), help="chunked: cache dtype")
     ap.add_argument("--fixed-len", type=int, default=0,
                     help="llama8b: every row this long instead of uniform 512..8192 (a balance control)")
@@ -128,7 +130,7 @@ def build_workload(name: str, args=None):
     import workloads as W
 
     if name == "chunked":
-        w = W.chunked(context=args.context)
+        w = W.chunked(context=args.context, chunk=args.chunk)
         return {"fp8": W.scaled_fp8, "int8": W.scaled_int8}.get(args.kv, lambda x: x)(w)
     if name == "llama8b" and args is not None and args.fixed_len:
         return W.llama8b(min_len=args.fixed_len, max_len=args.fixed_len)
@@ -175,20 +177,15 @@ def run_chunked(args, w, device):
     mdl = max(lens[:nd])
     a = pk._args(cache, q, out, table, klens, max(lens), 0, args.decode_parts, None, cu_q=cu_q, num_decode=nd,
                  max_decode_kv_len=mdl, max_q_len=max(w.q_lens), total_q=q.shape[0])
+    a.prefill_parts = args.prefill_parts
     ws = torch.empty(max(16, pk.paged_attn_workspace_size(cache, a)), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
 
     def step(i):
         pk.paged_attn_prefill_chunk(cache, q, cu_q, table, klens, max(lens), nd, max(w.q_lens), out=out,
                                     max_decode_kv_len=mdl, decode_parts=args.decode_parts, workspace=ws,
-                                    events=ev.handles(i))
+                                    events=ev.handles(i), prefill_parts=args.prefill_parts)
 
-    row0 = None
-    if w.kv_dtype in ("fp8", "int8") and not args.no_cpu_baseline:
-        # batch row 0 before any token is appended, for the drift report of the oracle leg
-        pk.paged_attn_decode(cache, q, d_table, d_lens, int(lens.max()), out=out, workspace=ws)
-        torch.cuda.synchronize()
-        row0 = out[0].float().cpu().numpy()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -264,6 +264,9 @@ typedef struct {
                                     many wavefronts (<= 4096, and at most one per 8 blocks of the
                                     head's work); 0 = auto (8 per compute unit in all, 12 for a
                                     one-byte cache) */
+    int32_t prefill_parts;       /* prefill: key ranges each tile of query rows is split into
+                                    (1..8; their states are merged by a second kernel);
+                                    0 = auto (enough workgroups for one per compute unit) */
     int32_t shared_prefix_blocks;/* decode only: the caller promises that the first
                                     shared_prefix_blocks entries of every row's block table are the
                                     same block ids (a prefix all rows share); the call then computes

@@ -76,6 +76,7 @@ class pkv_attn_args(ctypes.Structure):
                 ("cu_q", ctypes.c_void_p), ("num_decode", ctypes.c_int32),
                 ("max_decode_kv_len", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
                 ("total_q", ctypes.c_int32), ("decode_parts", ctypes.c_int32),
+                ("prefill_parts", ctypes.c_int32),
                 ("shared_prefix_blocks", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("events", ctypes.c_void_p * 4)]
@@ -558,7 +559,8 @@ def paged_attn_decode_noalloc(cache: KVCache, q, block_table, kv_lens, max_kv_le
 
 def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_kv_len: int, num_decode: int,
                              max_q_len: int, out=None, layer: int = 0, max_decode_kv_len: int = 0,
-                             decode_parts: int = 0, workspace=None, stream=None, events=None):
+                             decode_parts: int = 0, workspace=None, stream=None, events=None,
+                             prefill_parts: int = 0):
     """q [total_q, Hq, 128]; rows 0..num_decode-1 are decode rows (cu_q[i] = i)."""
     ts = _torch_stream(stream, q.device)
     if out is None:
@@ -566,6 +568,7 @@ def paged_attn_prefill_chunk(cache: KVCache, q, cu_q, block_table, kv_lens, max_
     a = _args(cache, q, out, block_table, kv_lens, max_kv_len, layer, decode_parts, workspace, cu_q=cu_q,
               num_decode=num_decode, max_decode_kv_len=max_decode_kv_len, max_q_len=max_q_len,
               total_q=q.shape[0])
+    a.prefill_parts = prefill_parts
     _set_events(a, events)
     keep = _with_workspace(cache, a, workspace, q.device, ts)  # noqa: F841 (stream-ordered reuse)
     _check(_lib.paged_attn_prefill_chunk(ctypes.byref(cache.desc), ctypes.byref(a), _stream(ts)))

@@ -52,6 +52,8 @@ int check_attn(const pkv_cache* c, const pkv_attn_args* a) {
                     a->max_kv_len);
     if (a->decode_parts < 0 || a->decode_parts > 4096)
         return fail(PKV_ERR_INVALID, "decode_parts %d must be in [0, 4096]", a->decode_parts);
+    if (a->prefill_parts < 0 || a->prefill_parts > 8)
+        return fail(PKV_ERR_INVALID, "prefill_parts %d must be in [0, 8]", a->prefill_parts);
     const uintptr_t align = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->out) |
                             reinterpret_cast<uintptr_t>(c->k_pool) | reinterpret_cast<uintptr_t>(c->v_pool) |
                             reinterpret_cast<uintptr_t>(a->workspace);

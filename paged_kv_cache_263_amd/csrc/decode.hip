@@ -1088,9 +1088,14 @@ int paged_attn_workspace_size(const pkv_cache* c, const pkv_attn_args* a, size_t
     if (st) return st;
     if (a->num_seqs == 0) return PKV_OK;
     // A prefill call uses the decode path for its decode rows; its chunk rows
-    // need no workspace.
+    // need the states of their key ranges when the tiles are split (after the
+    // decode part, 256-byte aligned).
     const int32_t rows = a->cu_q ? a->num_decode : a->num_seqs;
     *bytes = pkv::decode_workspace_bytes(c, a, rows);
+    if (a->cu_q) {
+        const size_t pre = pkv::prefill_workspace_bytes(c, a);
+        if (pre > 0) *bytes = (*bytes + 255) / 256 * 256 + pre;
+    }
     return PKV_OK;
 }
 

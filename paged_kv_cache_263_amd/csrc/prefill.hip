@@ -9,30 +9,50 @@
 // run on the matrix cores with shapes the hardware takes whole ([P1] "Kernel
 // engineering: the layer underneath everything else here" on tile shapes).
 //
-// Work decomposition: one workgroup (4 waves) per (chunk row, kv head, tile
-// of query rows).  A query row is one (token, query head) pair; the G heads of
-// one kv head share its K/V, so a tile holds 128 / G consecutive tokens with
-// all G heads each (128 rows), and wave w owns rows 32 w .. 32 w + 31 (row n
-// is token n / G, head n % G).  Per iteration the workgroup gathers 64 keys
-// (4 blocks, through the block table) into LDS - K as [key][d] with rows
-// padded to 136 elements, V as [d][16 tokens] tiles with the two 8-token
-// halves of a row swapped on alternate groups of 8 rows (both layouts keep the
-// operand reads free of bank conflicts) - double buffered, one barrier per
-// iteration.  Each
-// wave then computes, on the 32x32x16 bf16 matrix instruction:
+// Work decomposition: one workgroup (8 waves) per (chunk row, tile of query
+// rows, key range, kv head).  A query row is one (token, query head) pair; the
+// G heads of one kv head share its K/V, so a tile holds 256 / G consecutive
+// tokens with all G heads each (256 rows), and wave w owns rows 32 w .. 32 w +
+// 31 (row n is token n / G, head n % G).  Per iteration the workgroup walks 64
+// keys (4 blocks, gathered through the block table) staged in LDS - K as
+// [key][d] with rows padded to 136 elements, V as [d][16 tokens] tiles with
+// the two 8-token halves of a row swapped on alternate groups of 8 rows (both
+// layouts keep the operand reads free of bank conflicts).  Each wave computes,
+// on the 32x32x16 bf16 matrix instruction:
 //   S^T[64 keys x 32 rows] = K . Q^T        (2 key tiles x 8 steps over d)
 //   O^T[128 x 32 rows]    += V^T . P^T      (4 d tiles x 4 steps of 16 keys)
-// The lane holding a score column keeps that row's softmax state: running
-// max (rescaled lazily, only when a score passes it by 2^8) and normaliser.
-// The rows of K fed to the score product are permuted (bits 2 and 3 of the
-// key index swapped), so that the score registers come out holding, for each
+// and between the two the online softmax of its 64 x 32 scores (exponentials,
+// maxima, the bf16 rounding of P and the normaliser), which costs the vector
+// unit about as long as the products cost the matrix unit.
+//
+// Ping-pong.  The 8 waves form two groups of 4, one wave of each group per
+// SIMD.  Workgroup barriers cut the iterations into phases in which one group
+// issues matrix products (P.V of iteration i and K.Q^T of iteration i + 1)
+// while the other runs its softmax, and the groups swap at every barrier, so
+// the matrix and vector work of a SIMD overlap instead of following each
+// other.  Group 0 stages the K tiles and group 1 the V tiles, each in its
+// softmax phase, from registers loaded two phases earlier; two LDS buffers for
+// K and two for V are enough for this order (a buffer is rewritten only after
+// both groups have read it).  One staged tile serves 256 query rows.
+//
+// The lane holding a score column keeps that row's softmax state: running max
+// (rescaled lazily, only when a score passes it by 2^8) and normaliser.  The
+// rows of K fed to the score product are permuted (bits 2 and 3 of the key
+// index swapped), so that the score registers come out holding, for each
 // 16-key step, exactly the 8 consecutive keys the P.V operand of that lane
 // needs: P goes from the score registers to the second product with no lane
-// exchange, and V is read in the cache's token order.  P is rounded to bf16 once;
-// the normaliser sums the same rounded values (bf16 dot products with 1.0),
-// so the rounding largely cancels between numerator and denominator.
+// exchange, and V is read in the cache's token order.  P is rounded to bf16
+// once; the normaliser sums the same rounded values (bf16 dot products with
+// 1.0), so the rounding largely cancels between numerator and denominator.
 // fp8 and int8 caches are converted to bf16 while staging (exact) with the
 // per-head scales folded into the score scale and the output.
+//
+// Key ranges.  When the tiles alone would leave compute units idle, each tile's
+// keys are split into ranges (whole iterations); a range's state (unnormalised
+// output, running max, normaliser) goes to the workspace and a merge kernel
+// combines the ranges of every query with the max/normaliser algebra of the
+// online softmax.  The same mode, without the causal mask, computes the decode
+// rows' states over a prefix all rows share (the shared-prefix pass).
 #include <cmath>
 
 #include <cstdlib>
@@ -48,12 +68,14 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
 
 namespace {
 
-constexpr int kRows = 128;             // query rows per workgroup (4 waves x 32)
+constexpr int kThreads = 512;          // 8 waves: two groups of 4, one wave of each per SIMD
+constexpr int kRows = 256;             // query rows per workgroup (8 waves x 32)
 constexpr int kKeys = 64;              // keys per iteration (4 blocks)
 constexpr int kKStride = kD + 8;       // padded K row (elements)
 constexpr int kKStage = kKeys * kKStride;  // elements of one K stage
 constexpr int kVStage = 4 * kTile;         // elements of one V stage (4 tiles [128][16])
 constexpr float kLazy = 8.0f;              // rescale threshold (log2 units)
+constexpr int kMaxParts = 8;               // key ranges per tile
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -69,19 +91,22 @@ struct PrefillParams {
     const int32_t* cu_q;    // [num_seqs + 1]
     int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, max_q_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
+    // key ranges per tile; with parts > 1 (or in the shared-prefix pass) the
+    // state of (range, query, head) goes to states[part][query][hq][kState]
+    // instead of the output, query = the global query index (the decode row
+    // in the shared-prefix pass)
+    float* states;
+    int32_t parts;
     // shared-prefix pass (PREFIX kernels): the decode rows' queries (one per
     // row, total_q rows) over the first prefix_tokens keys of table row 0, no
-    // causal mask, the keys split into prefix_parts ranges of whole
-    // iterations; the state of (part, row, head) goes to
-    // states[part][row][hq][kPrefixState]
-    float* states;
-    int32_t prefix_tokens, prefix_parts;
+    // causal mask
+    int32_t prefix_tokens;
 };
 
-// Floats of one (row, query head) shared-prefix state: unnormalised output
-// [128], running max (log2 units), normaliser, padding (the decode kernel
-// reads the same layout).
-constexpr int kPrefixState = kD + 4;
+// Floats of one (query, head) state: unnormalised output [128], running max
+// (log2 units), normaliser, padding (the decode kernel reads the same layout
+// for the shared-prefix states).
+constexpr int kState = kD + 4;
 
 // LDS element offset of tokens 8 h .. 8 h + 7 of d row d inside a staged V
 // tile: rows of 16 tokens, the two halves swapped in rows with bit 3 of d
@@ -89,49 +114,69 @@ constexpr int kPrefixState = kD + 4;
 // cover all 64 banks.
 __device__ __forceinline__ int v_lds_offset(int d, int h) { return d * kBS + 8 * (h ^ ((d >> 3) & 1)); }
 
-// bf16 V piece staged by thread t: a permutation of the pieces inside each
-// wave's contiguous 1 KiB of the tile (so the global load stays one
-// contiguous run per wave), chosen so that every 16 lanes of the two 8-byte
-// LDS stores below write distinct banks.  Lane 16 a + b takes d row
+// bf16 V piece staged by thread u of the V group: a permutation of the pieces
+// inside each wave's contiguous 1 KiB of the tile (so the global load stays
+// one contiguous run per wave), chosen so that every 16 lanes of the two
+// 8-byte LDS stores below write distinct banks.  Lane 16 a + b takes d row
 // r = 4 a + b % 4 (and r + 16) of the wave's 32 rows, token group
 // g = 2 h + (b / 4) % 2 with h = (b / 8) ^ (a / 2).
 struct VPiece {
     int r, g;
 };
-__device__ __forceinline__ VPiece v_piece(int t) {
-    const int a = (t >> 4) & 3, b = t & 15;
+__device__ __forceinline__ VPiece v_piece(int u) {
+    const int a = (u >> 4) & 3, b = u & 15;
     const int r = 4 * a + (b & 3);
     const int h = ((b >> 3) & 1) ^ (a >> 1);
     return VPiece{r, 2 * h + ((b >> 2) & 1)};
 }
 
-// Staging registers for one iteration: thread t owns 16 bytes of each of the
-// iteration's 4 K tiles and 4 V tiles.  bf16 tiles (bf16_k_offset,
-// bf16_v_offset): K piece t, token t%16, d 8(t/16)..+7; V piece
-// 64 (t/64) + 16 g + r (v_piece), tokens 4g..4g+3 of d rows 32(t/64) + r and
-// that + 16; 256 threads read each 4 KiB tile contiguously.
-// One-byte tiles: K row t/16, elements (t%16)*8..+7, and V d row t/2, tokens
-// (t%2)*8..+7, their codes converted to bf16 on load.
-// The tile addresses are uniform (one per block) and the thread's offset
-// inside a tile is fixed, so a load costs no vector arithmetic.
+// Staging registers of one iteration's tiles: 16 bytes of each of the 4
+// tiles per thread.  The K group (threads u = 0..255 of group 0) holds K
+// tiles, the V group V tiles, in the same registers.
+//
+// K (k_load, k_store): bf16 tiles (bf16_k_offset): piece u, token u % 16, d
+// 8 (u / 16) .. +7, so the group reads each 4 KiB tile contiguously.
+// One-byte tiles: row u / 16, codes (u % 16) * 8 .. +7, converted to bf16 on
+// load.  Tile addresses are uniform (one per block) and the thread's offset
+// inside a tile is fixed.
 template <int KV>
 struct Stage {
-    u32x4_t k[4], v[4];
-    // voff: this thread's V piece (bf16); one-byte tiles keep it as two 4-byte
-    // words at voff and voff1 (byte_v_offset)
-    __device__ __forceinline__ void load(const char* const kb[4], const char* const vb[4], uint32_t koff,
-                                         uint32_t voff, uint32_t voff1) {
+    u32x4_t k[4];
+    __device__ __forceinline__ void k_load(const char* const kb[4], uint32_t koff) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if constexpr (KV == PKV_BF16) {
                 k[b] = ld<u32x4_t>(kb[b] + koff);
-                v[b] = ld<u32x4_t>(vb[b] + voff);
             } else {
                 const u32x2_t kk = ld<u32x2_t>(kb[b] + koff);
-                const u32x2_t vv = {ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1)};
                 const u32x2_t k0 = byte4_to_bf16x4<KV>(kk[0]), k1 = byte4_to_bf16x4<KV>(kk[1]);
-                const u32x2_t v0 = byte4_to_bf16x4<KV>(vv[0]), v1 = byte4_to_bf16x4<KV>(vv[1]);
                 k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
+            }
+        }
+    }
+    __device__ __forceinline__ void k_store(uint16_t* ks, int u) const {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if constexpr (KV == PKV_BF16)
+                st<u32x4_t>(ks + (b * kBS + (u & 15)) * kKStride + 8 * (u >> 4), k[b]);
+            else
+                st<u32x4_t>(ks + (b * kBS + (u >> 4)) * kKStride + (u & 15) * 8, k[b]);
+        }
+    }
+
+    // V (v_load, v_store): bf16 (bf16_v_offset): piece 64 (u / 64) + 16 g + r
+    // (v_piece), tokens 4g..4g+3 of d rows 32 (u / 64) + r and that + 16.
+    // One-byte tiles: d row u / 2, tokens (u % 2) * 8 .. +7, as two 4-byte
+    // words at voff and voff1 (byte_v_offset).
+    __device__ __forceinline__ void v_load(const char* const vb[4], uint32_t voff, uint32_t voff1) {
+        u32x4_t* v = k;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if constexpr (KV == PKV_BF16) {
+                v[b] = ld<u32x4_t>(vb[b] + voff);
+            } else {
+                const u32x2_t vv = {ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1)};
+                const u32x2_t v0 = byte4_to_bf16x4<KV>(vv[0]), v1 = byte4_to_bf16x4<KV>(vv[1]);
                 v[b] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
             }
         }
@@ -139,33 +184,33 @@ struct Stage {
     // Zero V of tokens at or past valid[b] (the row's partial last block and
     // blocks past its end, which hold whatever the clamped load read; 0 * NaN
     // is NaN).  Only the iteration that reaches the row's end calls this.
-    __device__ __forceinline__ void mask_tail(const int valid[4], int t) {
+    __device__ __forceinline__ void mask_tail(const int valid[4], int u) {
+        u32x4_t* v = k;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 // token of element e
-                const int tok = KV == PKV_BF16 ? 4 * v_piece(t).g + (e & 3) : (t & 1) * 8 + e;
+                const int tok = KV == PKV_BF16 ? 4 * v_piece(u).g + (e & 3) : (u & 1) * 8 + e;
                 if (tok >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
             }
             v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
     }
-    __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs, int t) const {
+    __device__ __forceinline__ void v_store(uint16_t* vs, int u) const {
+        const u32x4_t* v = k;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if constexpr (KV == PKV_BF16) {
-                st<u32x4_t>(ks + (b * kBS + (t & 15)) * kKStride + 8 * (t >> 4), k[b]);
-                const VPiece vp = v_piece(t);
+                const VPiece vp = v_piece(u);
                 const int g = vp.g;
-                const int d0 = 32 * (t >> 6) + vp.r;
+                const int d0 = 32 * (u >> 6) + vp.r;
                 uint16_t* vt = vs + b * kTile + 4 * (g & 1);
                 st<u32x2_t>(vt + v_lds_offset(d0, g >> 1), u32x2_t{v[b][0], v[b][1]});
                 st<u32x2_t>(vt + v_lds_offset(d0 + 16, g >> 1), u32x2_t{v[b][2], v[b][3]});
             } else {
-                st<u32x4_t>(ks + (b * kBS + (t >> 4)) * kKStride + (t & 15) * 8, k[b]);
-                st<u32x4_t>(vs + b * kTile + v_lds_offset(t >> 1, t & 1), v[b]);
+                st<u32x4_t>(vs + b * kTile + v_lds_offset(u >> 1, u & 1), v[b]);
             }
         }
     }
@@ -182,25 +227,42 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// PREFIX: the shared-prefix pass of a decode call (see PrefillParams); else a
-// chunked-prefill row.
+// Workgroup barrier that orders LDS only: the stores before it are complete
+// (lgkmcnt) and no LDS access moves across it, while global loads issued
+// before it stay in flight (the staging loads run two phases ahead).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// PREFIX: the shared-prefix pass of a decode call (see PrefillParams); else
+// chunked-prefill rows.
 template <int KV, bool PREFIX>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
+    __shared__ int broken[kRows];
     constexpr int kElt = (KV == PKV_BF16) ? 2 : 1;
 
     const int t = threadIdx.x;
     const int wave = t >> 6;
+    // 0: stages K, starts with the matrix phase; 1: stages V.  Read through
+    // readfirstlane so the compiler sees a wave-uniform value and branches on
+    // it with scalar branches, each group's phases compiled as straight code.
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+    const int u = t & 255;      // thread index within its group
     const int lane = t & 63;
     const int c32 = lane & 31;  // score column = query row within the wave
     const int g = lane >> 5;    // lane group
-    // blockIdx -> (row, q tile, kv head), kv head fastest (one kv head per XCD).
-    const int per_row = p.q_tiles * p.hkv;
+    // blockIdx -> (row, q tile, key range, kv head), kv head fastest (one kv
+    // head per XCD: the workgroups of one head share its K/V in that L2).
+    const int per_row = p.q_tiles * p.parts * p.hkv;
     const int row = PREFIX ? 0 : p.row0 + blockIdx.x / per_row;
     const int kvh = blockIdx.x % p.hkv;
-    const int qt = PREFIX ? blockIdx.x / (p.hkv * p.prefix_parts) : (blockIdx.x % per_row) / p.hkv;
-    const int part = PREFIX ? (blockIdx.x / p.hkv) % p.prefix_parts : 0;
+    const int part = (blockIdx.x / p.hkv) % p.parts;
+    const int qt = (blockIdx.x % per_row) / (p.hkv * p.parts);
+    const bool split = PREFIX || p.parts > 1;  // states to the workspace, not outputs
 
     const int qbeg = PREFIX ? 0 : p.cu_q[row];
     const int C = PREFIX ? p.total_q : p.cu_q[row + 1] - qbeg;
@@ -214,29 +276,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     const bool over = !PREFIX && C > p.max_q_len;
     const bool row_ok = PREFIX ? L >= kBS
                                : C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS && !over;
-    if (!PREFIX && C > covered && qt == p.q_tiles - 1) {
-        const u32x4_t nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};  // bf16 NaN x 8
-        const int pieces = (C - covered) * p.group * (kD / 8);
-        for (int e = t; e < pieces; e += 256) {
-            const int tok_e = covered + e / (p.group * (kD / 8));
-            const int rest = e % (p.group * (kD / 8));
-            uint16_t* o = static_cast<uint16_t*>(p.out) +
-                          (static_cast<int64_t>(qbeg + tok_e) * p.hq + kvh * p.group + rest / (kD / 8)) * kD +
-                          8 * (rest % (kD / 8));
-            st<u32x4_t>(o, nan8);
+    if (!PREFIX && C > covered && qt == p.q_tiles - 1 && part == 0) {
+        // bf16 NaN x 8 into the output, or NaN states (normaliser NaN) when
+        // the ranges are merged later
+        const u32x4_t nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+        const int per_tok = p.group * (split ? 1 : kD / 8);
+        const int pieces = (C - covered) * per_tok;
+        for (int e = t; e < pieces; e += kThreads) {
+            const int tok_e = covered + e / per_tok;
+            const int rest = e % per_tok;
+            const int64_t q_h = static_cast<int64_t>(qbeg + tok_e) * p.hq + kvh * p.group;
+            if (split) {
+                st<float2>(p.states + (q_h + rest) * kState + kD, float2{0.f, __builtin_nanf("")});
+            } else {
+                uint16_t* o = static_cast<uint16_t*>(p.out) + (q_h + rest / (kD / 8)) * kD + 8 * (rest % (kD / 8));
+                st<u32x4_t>(o, nan8);
+            }
         }
     }
     // Prefix pass: the caller promises that every row's table starts with
     // row 0's first prefix_tokens / 16 block ids.  Each workgroup checks the
     // promise for its own rows; a row that breaks it gets a NaN state, so its
     // output is NaN like that of any other invalid row.
-    __shared__ int broken[kRows];
     if constexpr (PREFIX) {
-        for (int i = t; i < p.tile_tokens; i += 256) broken[i] = 0;
+        for (int i = t; i < p.tile_tokens; i += kThreads) broken[i] = 0;
         __syncthreads();
         const int S = p.prefix_tokens / kBS;
         const int ntok = min(p.tile_tokens, C - j0);
-        for (int e = t; e < ntok * S; e += 256) {
+        for (int e = t; e < ntok * S; e += kThreads) {
             const int r = e / S, b = e - r * S;
             if (p.table[static_cast<int64_t>(j0 + r) * p.max_blocks + b] != p.table[b]) broken[r] = 1;
         }
@@ -280,7 +347,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     }
 
     float m = -INFINITY;  // reference max (log2 units), same in both lane groups
-    float l = 0.f;        // this lane's part of the normaliser
     f32x16_t acc[4];      // O^T d tiles: d = 32 dt + 8 (i / 4) + 4 g + i % 4
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -290,10 +356,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
     const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
     const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
-    const uint32_t koff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : ((t >> 4) * kD + (t & 15) * 8) * kElt);
+    const uint32_t koff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * u : ((u >> 4) * kD + (u & 15) * 8) * kElt);
     const uint32_t voff = static_cast<uint32_t>(
-        KV == PKV_BF16 ? 16 * (64 * (t >> 6) + 16 * v_piece(t).g + v_piece(t).r) : byte_v_offset(t >> 1, (t & 1) * 8));
-    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(t >> 1, (t & 1) * 8 + 4));
+        KV == PKV_BF16 ? 16 * (64 * (u >> 6) + 16 * v_piece(u).g + v_piece(u).r) : byte_v_offset(u >> 1, (u & 1) * 8));
+    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(u >> 1, (u & 1) * 8 + 4));
     // LDS element offsets of this lane's operands
     const int krow0 = key_row(c32) * kKStride + 8 * g;  // + (32 kt) * kKStride + 16 sd
     const int vrow0 = v_lds_offset(c32, g);             // + b * kTile + (32 dt) * kBS
@@ -303,9 +369,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // keys are masked); a block id outside the pool reads block 0 and makes
     // the output NaN.
     bool bad = false;
-    auto stage_load = [&](Stage<KV>& sr, int it) {
-        const char* kb[4];
-        const char* vb[4];
+    auto tiles = [&](int it, const char* const pool, const char* tb[4]) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int lb = min(it * 4 + b, nblk_seq - 1);
@@ -314,27 +378,51 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
                 bad = bad || lb >= 0;
                 id = 0;
             }
-            kb[b] = kpool + id * blk_bytes;
-            vb[b] = vpool + id * blk_bytes;
+            tb[b] = pool + id * blk_bytes;
         }
-        sr.load(kb, vb, koff, voff, voff1);
     };
-    auto stage_store = [&](Stage<KV>& sr, int it, int buf) {
+    Stage<KV> sr;
+    auto k_load = [&](int it) {
+        const char* kb[4];
+        tiles(it, kpool, kb);
+        sr.k_load(kb, koff);
+    };
+    auto v_load = [&](int it) {
+        const char* vb[4];
+        tiles(it, vpool, vb);
+        sr.v_load(vb, voff, voff1);
+    };
+    auto k_store = [&](int it) { sr.k_store(ks[it & 1], u); };
+    auto v_store = [&](int it) {
         if ((it + 1) * kKeys > L) {  // the iteration that reaches the row's end
             int valid[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) valid[b] = min(kBS, max(0, L - (it * 4 + b) * kBS));
-            sr.mask_tail(valid, t);
+            sr.mask_tail(valid, u);
         }
-        sr.store(ks[buf], vs[buf], t);
+        sr.v_store(vs[it & 1], u);
     };
 
-    // one iteration over the 64 keys staged in LDS buffer buf
-    auto compute = [&](int it, int buf) {
-        const uint16_t* kc = ks[buf] + krow0;
-        const uint16_t* vc = vs[buf] + vrow0;
-        const int kbase = it * kKeys;
-        f32x16_t s[2];
+    // Scores of the iteration this wave works on, and its P operand: step
+    // (kt, h) covers keys 32 kt + 16 h + 8 g .. +7 (block 2 kt + h).
+    f32x16_t s[2];
+    u32x4_t pk[2][2];
+    // The scheduling barriers at the end of qk and pv keep each operand read
+    // four products ahead of its use: in its matrix phase this wave is the
+    // only one issuing products on its SIMD, so nothing else hides the LDS
+    // latency.
+    auto prefetch4 = [] {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads
+#pragma unroll
+        for (int n = 0; n < 12; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read four ahead
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // S^T = K . Q^T over the 64 keys of iteration it (K in buffer it & 1)
+    auto qk = [&](int it) {
+        const uint16_t* kc = ks[it & 1] + krow0;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -347,54 +435,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[sd], s[kt], 0, 0, 0);
             }
         }
-        // online softmax.  Scores stay unscaled until the exponent (scale >
-        // 0, so the maximum commutes with it); keys can pass a query's
-        // position only in the iterations that reach the diagonal, so only
-        // those take the masked path (a uniform branch).
-        float x[32];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[16 * kt + i] = s[kt][i];
-        if (kbase + kKeys - 1 > first_pos) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (kbase + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7) > qpos) x[16 * kt + i] = -INFINITY;
-        }
-        float mb = x[0];
-#pragma unroll
-        for (int i = 1; i < 31; i += 2) mb = fmaxf(fmaxf(mb, x[i]), x[i + 1]);
-        mb = fmaxf(mb, x[31]) * scale;
-        if (__any(mb > m + kLazy)) {  // rare: a new maximum for some row
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float mn = fmaxf(m, mb);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-            m = mn;
-        }
-        const float neg_m = -m;
-        // P^T operand of step (kt, h): keys 32 kt + 16 h + 8 g .. +7
-        u32x4_t pk[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float pr[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pr[e] = __builtin_amdgcn_exp2f(fmaf(x[16 * kt + 8 * h + e], scale, neg_m));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = pack_bf16(pr[2 * e], pr[2 * e + 1]);
-                    pk[kt][h][e] = w;
-                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l, false);
-                }
-            }
-        // O^T += V^T . P^T: step (kt, h) covers block 2 kt + h
+        prefetch4();
+    };
+    // O^T += V^T . P^T over iteration it's 64 keys (V in buffer it & 1)
+    auto pv = [&](int it) {
+        const uint16_t* vc = vs[it & 1] + vrow0;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -407,35 +452,139 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
                 }
             }
+        prefetch4();
+    };
+    // Online softmax of iteration it's scores (in place in s) into pk.
+    // Scores stay unscaled until the exponent (scale > 0, so the maximum
+    // commutes with it); keys can pass a query's position only in the
+    // iterations that reach the diagonal, so only those take the masked path
+    // (a uniform branch).  The maximum and the normaliser are accumulated in
+    // four independent chains (one per 16-key step), so that one wave's
+    // dependent instructions do not wait on each other.
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's normaliser, per step
+    auto softmax = [&](int it) {
+        const int kbase = it * kKeys;
+        if (kbase + kKeys - 1 > first_pos) {
+            // score (kt, i) is key kbase + 8 g + c with c = 32 kt + 16 (i / 8) + i % 8
+            const int last = qpos - kbase - 8 * g;  // the largest visible c
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kt + 16 * (i >> 3) + (i & 7) > last) s[kt][i] = -INFINITY;
+        }
+        float mc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int kt = c >> 1, o = 8 * (c & 1);
+            float x = fmaxf(s[kt][o], s[kt][o + 1]);
+#pragma unroll
+            for (int e = 2; e < 8; e += 2) x = fmaxf(fmaxf(x, s[kt][o + e]), s[kt][o + e + 1]);
+            mc[c] = x;
+        }
+        float mb = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])) * scale;
+        // A row can still have seen no key at all (m = -inf): in a key range
+        // past its diagonal every score is masked.  Its state stays (-inf, 0,
+        // 0) and contributes nothing when the ranges are merged.
+        if (__any(mb > m + kLazy)) {  // rare: a new maximum for some row
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = fmaxf(m, mb);
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) lp[c] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+            m = mn;
+        }
+        const float neg_m = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * h + 2 * e], scale, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * h + 2 * e + 1], scale, neg_m));
+                    const uint32_t w = pack_bf16(p0, p1);
+                    pk[kt][h][e] = w;
+                    lp[2 * kt + h] =
+                        __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, lp[2 * kt + h], false);
+                }
+            }
     };
 
-    // One register stage and two LDS buffers: the loads for iteration it + 1
-    // are issued before iteration it is computed and stored to the other LDS
-    // buffer after it.  The loads are unconditional (clamped iteration), so no
-    // branch sits between a load and its use.
-    // (a prefix-pass workgroup walks its part's range of iterations)
-    const int it_begin = PREFIX ? static_cast<int>(static_cast<int64_t>(n_iter) * part / p.prefix_parts) : 0;
-    const int it_end = PREFIX ? static_cast<int>(static_cast<int64_t>(n_iter) * (part + 1) / p.prefix_parts) : n_iter;
-    Stage<KV> sreg;
-    const int last = max(it_end - 1, it_begin);
-    stage_load(sreg, it_begin);
-    if (it_end > it_begin) stage_store(sreg, it_begin, 0);
-    __syncthreads();
-    for (int it = it_begin; it < it_end; ++it) {
-        const int cur = (it - it_begin) & 1;
-        stage_load(sreg, min(it + 1, last));
-        compute(it, cur);
-        if (it + 1 < it_end) stage_store(sreg, it + 1, cur ^ 1);
-        __syncthreads();
+    // The workgroup's iterations: its key range of the tile's n_iter.
+    const int ib = static_cast<int>(static_cast<int64_t>(n_iter) * part / p.parts);
+    const int ie = static_cast<int>(static_cast<int64_t>(n_iter) * (part + 1) / p.parts);
+    // Schedule (phases end at a barrier; group 0 = A, group 1 = B):
+    //   prologue: A stages K(ib), K(ib+1) and loads K(ib+2); B stages V(ib) and loads V(ib+1)
+    //   P0: A: qk(ib)
+    //   P1: A: softmax(ib)                           B: qk(ib)
+    //   for it = ib .. ie-1:
+    //     a: A: qk(it+1), pv(it)                       B: softmax(it), store V(it+1), load V(it+2)
+    //     b: A: softmax(it+1), store K(it+2), load K(it+3)   B: qk(it+1), pv(it)
+    // K(x) lands in ks[x & 1] in phase b of iteration x - 2, after both groups
+    // read K(x - 2) (B in phase b of iteration x - 3); V(x) lands in vs[x & 1]
+    // in phase a of iteration x - 1, after both read V(x - 2) (B in phase b of
+    // iteration x - 2).  Every wave passes the same barriers.
+    // Each group runs its own loop (straight code per phase for the
+    // compiler); both pass the same barriers.
+    if (ie > ib) {
+        if (grp == 0) {
+            k_load(ib);
+            k_store(ib);
+            if (ib + 1 < ie) {
+                k_load(ib + 1);
+                k_store(ib + 1);
+            }
+            if (ib + 2 < ie) k_load(ib + 2);
+            lds_barrier();
+            qk(ib);
+            lds_barrier();
+            softmax(ib);
+            lds_barrier();
+            for (int it = ib; it < ie; ++it) {
+                if (it + 1 < ie) qk(it + 1);
+                pv(it);
+                lds_barrier();
+                if (it + 1 < ie) softmax(it + 1);
+                if (it + 2 < ie) {
+                    k_store(it + 2);
+                    if (it + 3 < ie) k_load(it + 3);
+                }
+                lds_barrier();
+            }
+        } else {
+            v_load(ib);
+            v_store(ib);
+            if (ib + 1 < ie) v_load(ib + 1);
+            lds_barrier();
+            lds_barrier();
+            qk(ib);
+            lds_barrier();
+            for (int it = ib; it < ie; ++it) {
+                softmax(it);
+                if (it + 1 < ie) v_store(it + 1);
+                if (it + 2 < ie) v_load(it + 2);
+                lds_barrier();
+                if (it + 1 < ie) qk(it + 1);
+                pv(it);
+                lds_barrier();
+            }
+        }
+    } else if constexpr (PREFIX) {
+        __syncthreads();  // (the promise check's flags)
     }
 
     bad = bad || !row_ok;
     if constexpr (PREFIX) bad = bad || (qrow_ok && broken[tok] != 0);
+    float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
     l += __shfl_xor(l, 32);
     if (!qrow_ok) return;
-    if constexpr (PREFIX) {  // the state, unnormalised (the decode kernel continues from it)
+    if (split) {  // the range's state, unnormalised (merged later)
         const float nan = __builtin_nanf("");
-        float* sp = p.states + ((static_cast<int64_t>(part) * p.total_q + j) * p.hq + kvh * p.group + hh) * kPrefixState;
+        const int64_t qi = PREFIX ? j : qbeg + j;
+        float* sp = p.states + ((static_cast<int64_t>(part) * p.total_q + qi) * p.hq + kvh * p.group + hh) * kState;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -460,27 +609,99 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         }
 }
 
+// Combines the key ranges of chunk queries q0 .. total_q - 1: for query q and
+// head h, with range k's state (acc_k, m_k, l_k) and M = max_k m_k, the output
+// is sum_k acc_k 2^(m_k - M) / sum_k l_k 2^(m_k - M), times v_scale of h's kv
+// head.  32 threads per (query, head), 4 d each; ranges in order.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillParams p, int q0) {
+    const int64_t qh = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);  // (q - q0) * hq + h
+    const int d = 4 * (threadIdx.x & 31);
+    if (qh >= static_cast<int64_t>(p.total_q - q0) * p.hq) return;
+    const int64_t q = q0 + qh / p.hq;
+    const int h = static_cast<int>(qh % p.hq);
+    const int64_t stride = static_cast<int64_t>(p.total_q) * p.hq * kState;
+    const float* s0 = p.states + (q * p.hq + h) * kState;
+    float mk[kMaxParts];
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) mk[k] = k < p.parts ? s0[k * stride + kD] : -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) mx = fmaxf(mx, mk[k]);
+    float lsum = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) {
+        if (k < p.parts) {
+            const float w = __builtin_amdgcn_exp2f(mk[k] - mx);
+            lsum += s0[k * stride + kD + 1] * w;
+            o += ld<f32x4_t>(s0 + k * stride + d) * w;
+        }
+    }
+    const float vscale = p.v_scale ? p.v_scale[h / p.group] : 1.f;
+    const float inv = vscale / lsum;
+    const uint32_t a = bf16_bits_rne(o[0] * inv) | (bf16_bits_rne(o[1] * inv) << 16);
+    const uint32_t b = bf16_bits_rne(o[2] * inv) | (bf16_bits_rne(o[3] * inv) << 16);
+    st<u32x2_t>(static_cast<uint16_t*>(p.out) + (q * p.hq + h) * kD + d, u32x2_t{a, b});
+}
+
+int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+// PKV_PREFIX_PARTS overrides the shared-prefix pass's key-range count for tuning runs.
+int env_int(const char* name) {
+    const char* e = std::getenv(name);
+    return e ? std::atoi(e) : 0;
+}
+
 }  // namespace
 
 // Key ranges the shared-prefix pass splits into: enough workgroups for one
-// per compute unit (measured on 256 rows: two ranges beat four by 5 us, as
-// each range's states are written and combined), each range at least one
-// 64-key iteration, at most 8.
+// per compute unit, each range at least one 64-key iteration, at most 8.
 int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {
     const int32_t group = a->num_q_heads / c->num_kv_heads;
     const int64_t tiles = static_cast<int64_t>((rows + kRows / group - 1) / (kRows / group)) * c->num_kv_heads;
     const int64_t iters = (static_cast<int64_t>(a->shared_prefix_blocks) * kBS + kKeys - 1) / kKeys;
-    static const int env = [] {  // PKV_PREFIX_PARTS overrides the count for tuning runs
-        const char* e = std::getenv("PKV_PREFIX_PARTS");
-        return e ? std::atoi(e) : 0;
-    }();
-    int64_t parts = env > 0 ? env : (256 + tiles - 1) / tiles;
-    parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+    static const int env = env_int("PKV_PREFIX_PARTS");
+    int64_t parts = env > 0 ? env : (device_cus() + tiles - 1) / tiles;
+    parts = parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts);
     return static_cast<int>(parts < iters ? parts : (iters < 1 ? 1 : iters));
 }
 
+// Key ranges per tile of a chunked-prefill launch: when the (row, q tile, kv
+// head) tiles are fewer than the compute units, enough ranges for one
+// workgroup per compute unit, each at least 8 iterations of the longest row,
+// at most 8.
+int prefill_parts(const pkv_cache* c, const pkv_attn_args* a) {
+    const int32_t n_pre = a->num_seqs - a->num_decode;
+    if (!a->cu_q || n_pre <= 0 || a->max_q_len <= 0) return 1;
+    if (a->prefill_parts > 0) return a->prefill_parts < kMaxParts ? a->prefill_parts : kMaxParts;
+    const int32_t group = a->num_q_heads / c->num_kv_heads;
+    const int32_t tile_tokens = kRows / group;
+    const int64_t tiles = static_cast<int64_t>(n_pre) * ((a->max_q_len + tile_tokens - 1) / tile_tokens) *
+                          c->num_kv_heads;
+    int64_t parts = (device_cus() + tiles - 1) / tiles;
+    const int64_t by_len = (static_cast<int64_t>(a->max_kv_len) + 8 * kKeys - 1) / (8 * kKeys);
+    if (parts > by_len) parts = by_len;
+    return static_cast<int>(parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts));
+}
+
+// Workspace of the chunk rows: range states when split (bytes).
+size_t prefill_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a) {
+    const int parts = prefill_parts(c, a);
+    if (parts <= 1) return 0;
+    return static_cast<size_t>(parts) * static_cast<size_t>(a->total_q) * a->num_q_heads * kState * sizeof(float);
+}
+
 // The shared-prefix pass of a decode call: every row's (query head) state over
-// the first 16 * S tokens of table row 0, into states [rows][hq][kPrefixState].
+// the first 16 * S tokens of table row 0, into states [parts][rows][hq][kState].
 int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, const void* q,
                          const int32_t* table, float* states, void* stream_ptr) {
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
@@ -510,14 +731,14 @@ int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t row
     p.scale_log2 = kLog2e / sqrtf(static_cast<float>(kD));
     p.states = states;
     p.prefix_tokens = a->shared_prefix_blocks * kBS;
-    p.prefix_parts = prefix_parts(c, a, rows);
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(q_tiles) * c->num_kv_heads * p.prefix_parts));
+    p.parts = prefix_parts(c, a, rows);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(q_tiles) * c->num_kv_heads * p.parts));
     if (c->kv_dtype == PKV_BF16)
-        hipLaunchKernelGGL((prefill_kernel<PKV_BF16, true>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<PKV_BF16, true>), grid, dim3(kThreads), 0, stream, p);
     else if (c->kv_dtype == PKV_FP8_E4M3)
-        hipLaunchKernelGGL((prefill_kernel<PKV_FP8_E4M3, true>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<PKV_FP8_E4M3, true>), grid, dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<PKV_INT8, true>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<PKV_INT8, true>), grid, dim3(kThreads), 0, stream, p);
     return PKV_OK;
 }
 
@@ -537,6 +758,14 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
         return fail(PKV_ERR_INVALID, "max_q_len must be positive and total_q must cover every row");
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // workspace: the decode rows' part, then the chunk rows' range states
+    const size_t dec_bytes = pkv::decode_workspace_bytes(c, a, a->num_decode);
+    const size_t pre_off = (dec_bytes + 255) / 256 * 256;
+    const size_t pre_bytes = pkv::prefill_workspace_bytes(c, a);
+    if (pre_bytes > 0 && (!a->workspace || a->workspace_bytes < pre_off + pre_bytes))
+        return fail(PKV_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", pre_off + pre_bytes,
+                    a->workspace ? a->workspace_bytes : 0);
+
     // decode rows: queries 0..num_decode-1, one per row
     const int32_t dec_len = a->max_decode_kv_len > 0 ? a->max_decode_kv_len : a->max_kv_len;
     if (dec_len > a->max_kv_len) return fail(PKV_ERR_INVALID, "max_decode_kv_len exceeds max_kv_len");
@@ -551,7 +780,8 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     const int32_t group = a->num_q_heads / c->num_kv_heads;
     const int32_t tile_tokens = pkv::kRows / group;
     const int32_t q_tiles = (a->max_q_len + tile_tokens - 1) / tile_tokens;
-    const int64_t grid = static_cast<int64_t>(n_pre) * q_tiles * c->num_kv_heads;
+    const int32_t parts = pkv::prefill_parts(c, a);
+    const int64_t grid = static_cast<int64_t>(n_pre) * q_tiles * parts * c->num_kv_heads;
     if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "prefill launch too large");
     const int64_t elt = c->kv_dtype == PKV_BF16 ? 2 : 1;
     const int64_t layer_elems = static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * pkv::kTile;
@@ -577,12 +807,21 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.total_q = a->total_q;
     p.tile_tokens = tile_tokens;
     p.scale_log2 = pkv::kLog2e / sqrtf(static_cast<float>(pkv::kD));
+    p.parts = parts;
+    p.states = parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pre_off) : nullptr;
+    const dim3 g1(static_cast<unsigned>(grid));
     if (c->kv_dtype == PKV_BF16)
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_BF16, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_BF16, false>), g1, dim3(pkv::kThreads), 0, s, p);
     else if (c->kv_dtype == PKV_FP8_E4M3)
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_FP8_E4M3, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_FP8_E4M3, false>), g1, dim3(pkv::kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_INT8, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_INT8, false>), g1, dim3(pkv::kThreads), 0, s, p);
+    if (parts > 1) {
+        // the chunk rows' queries are num_decode .. total_q - 1 (decode row i holds query i)
+        const int64_t pairs = static_cast<int64_t>(a->total_q - a->num_decode) * a->num_q_heads;
+        const dim3 mg(static_cast<unsigned>((pairs + 7) / 8));
+        hipLaunchKernelGGL(pkv::prefill_merge_kernel, mg, dim3(256), 0, s, p, a->num_decode);
+    }
     if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

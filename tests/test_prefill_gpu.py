@@ -12,11 +12,11 @@ from harness import TOL, HipSide, OracleSide, compare, q_offsets
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def check_prefill(w, tokens=None, heads=None, hip=None):
-    print(f"[case] {w.name} variant={w.variant} kv={w.kv_dtype} q_lens={w.q_lens[:6]}... hq={w.hq} hkv={w.hkv}",
-          flush=True)
+def check_prefill(w, tokens=None, heads=None, hip=None, parts=0):
+    print(f"[case] {w.name} variant={w.variant} kv={w.kv_dtype} q_lens={w.q_lens[:6]}... hq={w.hq} hkv={w.hkv} "
+          f"prefill_parts={parts}", flush=True)
     hip = hip or HipSide(w)
-    out = hip.prefill()
+    out = hip.prefill(prefill_parts=parts)
     torch.cuda.synchronize()
     orc = OracleSide(w)
     otable, olens = orc.pool.block_table(w.batch, hip.max_blocks)
@@ -39,10 +39,16 @@ def check_prefill(w, tokens=None, heads=None, hip=None):
 SMALL = [(0, 17), (5, 16), (100, 33), (0, 1), (1000, 64), (37, 200), (16, 15)]
 
 
+@pytest.mark.parametrize("parts", [0, 1, 4])
 @pytest.mark.parametrize("variant", ["plain", "peaked"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
-def test_small_chunks_with_decode_rows(kv, variant):
-    check_prefill(W.chunks(SMALL, hq=8, hkv=2, kv_dtype=kv, n_decode=3, variant=variant))
+def test_small_chunks_with_decode_rows(kv, variant, parts):
+    """Short chunks (1 to 200 queries over 0 to 1000 tokens of context) with
+    decode rows; each query tile whole (parts = 1), or its keys split into
+    ranges merged afterwards (auto: 3 here; 4), so that some ranges lie wholly
+    past a query's diagonal or hold no iteration."""
+    w = W.chunks(SMALL, hq=8, hkv=2, kv_dtype=kv, n_decode=3, variant=variant)
+    check_prefill(w, parts=parts)
 
 
 # group sizes G = Hq / Hkv: 8, 1, 16, 4, and the ones whose tiles leave rows
@@ -66,9 +72,19 @@ def chunked_workload(context, kv):
     return w
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
-def test_chunked_1024_over_16k_context_with_32_decodes(kv):
-    check_prefill(chunked_workload(16384, kv), tokens=CHUNK_TOKENS)
+@pytest.mark.parametrize("kv,parts", [("bf16", 0), ("fp8", 0), ("int8", 0), ("bf16", 3)])
+def test_chunked_1024_over_16k_context_with_32_decodes(kv, parts):
+    check_prefill(chunked_workload(16384, kv), tokens=CHUNK_TOKENS, parts=parts)
+
+
+@pytest.mark.parametrize("chunk,hq", [(512, 64), (1024, 32)])
+def test_chunk_split_over_key_ranges_at_64k(chunk, hq):
+    """Launches with fewer query tiles than compute units (a 512-query chunk
+    at eight heads per kv head, or a 1024-query chunk at four) split every
+    tile's 64K context into key ranges and merge them."""
+    w = W.chunked(context=65536, chunk=chunk, hq=hq)
+    w.variant = "peaked"
+    check_prefill(w, tokens=[t for t in CHUNK_TOKENS if t < chunk])
 
 
 @pytest.mark.parametrize("context,kv", [(32768, "bf16"), (65536, "bf16"), (131072, "bf16"), (65536, "fp8")])
