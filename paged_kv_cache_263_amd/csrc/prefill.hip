@@ -76,6 +76,8 @@ constexpr int kKStage = kKeys * kKStride;  // elements of one K stage
 constexpr int kVStage = 4 * kTile;         // elements of one V stage (4 tiles [128][16])
 constexpr float kLazy = 8.0f;              // rescale threshold (log2 units)
 constexpr int kMaxParts = 8;               // key ranges per tile
+constexpr int kPrefixThreads = 256;        // shared-prefix pass: 4 waves
+constexpr int kPrefixRows = 128;           // query rows per shared-prefix workgroup
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -91,15 +93,14 @@ struct PrefillParams {
     const int32_t* cu_q;    // [num_seqs + 1]
     int32_t row0, num_blocks, hkv, hq, group, max_blocks, max_kv_len, max_q_len, q_tiles, total_q, tile_tokens;
     float scale_log2;
-    // key ranges per tile; with parts > 1 (or in the shared-prefix pass) the
-    // state of (range, query, head) goes to states[part][query][hq][kState]
-    // instead of the output, query = the global query index (the decode row
-    // in the shared-prefix pass)
+    // key ranges per tile; with parts > 1 (and always in the shared-prefix
+    // pass) the state of (range, query, head) goes to
+    // states[part][query][hq][kState] instead of the output, query = the
+    // global query index (the decode row in the shared-prefix pass)
     float* states;
     int32_t parts;
-    // shared-prefix pass (PREFIX kernels): the decode rows' queries (one per
-    // row, total_q rows) over the first prefix_tokens keys of table row 0, no
-    // causal mask
+    // shared-prefix pass (prefix_kernel): the decode rows' queries over the
+    // first prefix_tokens keys of table row 0
     int32_t prefix_tokens;
 };
 
@@ -236,13 +237,11 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// PREFIX: the shared-prefix pass of a decode call (see PrefillParams); else
-// chunked-prefill rows.
-template <int KV, bool PREFIX>
+// Chunk rows of a prefill call.
+template <int KV>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
-    __shared__ int broken[kRows];
     constexpr int kElt = (KV == PKV_BF16) ? 2 : 1;
 
     const int t = threadIdx.x;
@@ -258,25 +257,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     // blockIdx -> (row, q tile, key range, kv head), kv head fastest (one kv
     // head per XCD: the workgroups of one head share its K/V in that L2).
     const int per_row = p.q_tiles * p.parts * p.hkv;
-    const int row = PREFIX ? 0 : p.row0 + blockIdx.x / per_row;
+    const int row = p.row0 + blockIdx.x / per_row;
     const int kvh = blockIdx.x % p.hkv;
     const int part = (blockIdx.x / p.hkv) % p.parts;
     const int qt = (blockIdx.x % per_row) / (p.hkv * p.parts);
-    const bool split = PREFIX || p.parts > 1;  // states to the workspace, not outputs
+    const bool split = p.parts > 1;  // states to the workspace, not outputs
 
-    const int qbeg = PREFIX ? 0 : p.cu_q[row];
-    const int C = PREFIX ? p.total_q : p.cu_q[row + 1] - qbeg;
+    const int qbeg = p.cu_q[row];
+    const int C = p.cu_q[row + 1] - qbeg;
     const int j0 = qt * p.tile_tokens;
     if (j0 >= C || qbeg < 0 || qbeg + C > p.total_q) return;  // (a malformed cu_q writes nothing)
-    // P: keys before the chunk (prefix pass: the prefix; every query sees all of it)
-    const int L = PREFIX ? p.prefix_tokens : p.kv_lens[row];
+    const int L = p.kv_lens[row];
     // a chunk row with more queries than max_q_len is invalid: every query of
     // it gets NaN, the last tile filling the queries that no tile owns
     const int covered = p.q_tiles * p.tile_tokens;
-    const bool over = !PREFIX && C > p.max_q_len;
-    const bool row_ok = PREFIX ? L >= kBS
-                               : C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS && !over;
-    if (!PREFIX && C > covered && qt == p.q_tiles - 1 && part == 0) {
+    const bool over = C > p.max_q_len;
+    const bool row_ok = C >= 1 && L >= C && L <= p.max_kv_len && L <= p.max_blocks * kBS && !over;
+    if (C > covered && qt == p.q_tiles - 1 && part == 0) {
         // bf16 NaN x 8 into the output, or NaN states (normaliser NaN) when
         // the ranges are merged later
         const u32x4_t nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
@@ -294,24 +291,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
             }
         }
     }
-    // Prefix pass: the caller promises that every row's table starts with
-    // row 0's first prefix_tokens / 16 block ids.  Each workgroup checks the
-    // promise for its own rows; a row that breaks it gets a NaN state, so its
-    // output is NaN like that of any other invalid row.
-    if constexpr (PREFIX) {
-        for (int i = t; i < p.tile_tokens; i += kThreads) broken[i] = 0;
-        __syncthreads();
-        const int S = p.prefix_tokens / kBS;
-        const int ntok = min(p.tile_tokens, C - j0);
-        for (int e = t; e < ntok * S; e += kThreads) {
-            const int r = e / S, b = e - r * S;
-            if (p.table[static_cast<int64_t>(j0 + r) * p.max_blocks + b] != p.table[b]) broken[r] = 1;
-        }
-        // (read after the barrier that follows the first stage store)
-    }
-    const int P = PREFIX ? L : L - C;
+    const int P = L - C;  // keys before the chunk
     const int jmax = min(j0 + p.tile_tokens, C);  // exclusive
-    const int kend = row_ok ? (PREFIX ? P : P + jmax) : 0;  // keys this tile needs
+    const int kend = row_ok ? P + jmax : 0;  // keys this tile needs
     const int n_iter = (kend + kKeys - 1) / kKeys;
     const int nblk_seq = (L + kBS - 1) / kBS;
     const int64_t blk_bytes = static_cast<int64_t>(p.hkv) * kTile * kElt;
@@ -324,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     const int hh = n - tok * p.group;
     const bool qrow_ok = tok < p.tile_tokens && j0 + tok < C;
     const int j = min(j0 + tok, C - 1);
-    const int qpos = PREFIX ? P - 1 : P + j;    // keys 0..qpos are visible
-    const int first_pos = PREFIX ? P - 1 : P + j0;  // the smallest qpos in the tile
+    const int qpos = P + j;        // keys 0..qpos are visible
+    const int first_pos = P + j0;  // the smallest qpos in the tile
 
     float scale = p.scale_log2;
     float vscale = 1.f;
@@ -572,18 +554,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
                 lds_barrier();
             }
         }
-    } else if constexpr (PREFIX) {
-        __syncthreads();  // (the promise check's flags)
     }
 
     bad = bad || !row_ok;
-    if constexpr (PREFIX) bad = bad || (qrow_ok && broken[tok] != 0);
     float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
     l += __shfl_xor(l, 32);
     if (!qrow_ok) return;
     if (split) {  // the range's state, unnormalised (merged later)
         const float nan = __builtin_nanf("");
-        const int64_t qi = PREFIX ? j : qbeg + j;
+        const int64_t qi = qbeg + j;
         float* sp = p.states + ((static_cast<int64_t>(part) * p.total_q + qi) * p.hq + kvh * p.group + hh) * kState;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -607,6 +586,228 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
                 bf16_bits_rne(acc[dt][4 * q4 + 2] * inv) | (bf16_bits_rne(acc[dt][4 * q4 + 3] * inv) << 16);
             st<u32x2_t>(op + 32 * dt + 8 * q4 + 4 * g, u32x2_t{a, b2});
         }
+}
+
+// The shared-prefix pass of a decode call: every decode row's query (one per
+// row, total_q rows) over the first prefix_tokens keys of table row 0, no
+// causal mask, the keys split into p.parts ranges of whole iterations; the
+// state of (range, row, head) goes to states[part][row][hq][kState].
+//
+// A pass over a 2000-token prefix gives each tile only tens of iterations, so
+// it uses smaller workgroups than the chunk rows: 4 waves (128 query rows,
+// 128 / G rows of the batch with all G heads), two per compute unit, one
+// barrier per iteration, every thread staging 16 bytes of each K and V tile
+// (one register stage, two LDS buffers) - the pipeline fill of the 8-wave
+// ping-pong costs more than it gains over so few iterations.  The products
+// and the softmax are the ones of the chunk kernel.
+template <int KV>
+__global__ __launch_bounds__(kPrefixThreads, 2) void prefix_kernel(const PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKStage];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][kVStage];
+    __shared__ int broken[kPrefixRows];
+    constexpr int kElt = (KV == PKV_BF16) ? 2 : 1;
+
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    const int lane = t & 63;
+    const int c32 = lane & 31;
+    const int g = lane >> 5;
+    // blockIdx -> (q tile, key range, kv head), kv head fastest
+    const int kvh = blockIdx.x % p.hkv;
+    const int part = (blockIdx.x / p.hkv) % p.parts;
+    const int qt = blockIdx.x / (p.hkv * p.parts);
+    const int C = p.total_q;
+    const int j0 = qt * p.tile_tokens;
+    if (j0 >= C) return;
+    const int L = p.prefix_tokens;
+    const bool row_ok = L >= kBS;
+
+    // The caller promises that every row's table starts with row 0's first
+    // prefix_tokens / 16 block ids.  Each workgroup checks the promise for its
+    // own rows; a row that breaks it gets a NaN state, so its output is NaN
+    // like that of any other invalid row.
+    for (int i = t; i < p.tile_tokens; i += kPrefixThreads) broken[i] = 0;
+    __syncthreads();
+    {
+        const int S = L / kBS;
+        const int ntok = min(p.tile_tokens, C - j0);
+        for (int e = t; e < ntok * S; e += kPrefixThreads) {
+            const int r = e / S, b = e - r * S;
+            if (p.table[static_cast<int64_t>(j0 + r) * p.max_blocks + b] != p.table[b]) broken[r] = 1;
+        }
+        // (read after the barrier that follows the first stage store)
+    }
+    const int n_iter = row_ok ? (L + kKeys - 1) / kKeys : 0;
+    const int nblk_seq = (L + kBS - 1) / kBS;
+    const int64_t blk_bytes = static_cast<int64_t>(p.hkv) * kTile * kElt;
+    const int32_t* trow = p.table;  // the prefix is row 0's
+
+    const int n = 32 * wave + c32;
+    const int tok = n / p.group;
+    const int hh = n - tok * p.group;
+    const bool qrow_ok = tok < p.tile_tokens && j0 + tok < C;
+    const int j = min(j0 + tok, C - 1);
+    const int last_key = L - 1;  // every row sees the whole prefix
+
+    float scale = p.scale_log2;
+    if constexpr (is_byte_dtype(KV)) scale *= p.k_scale[kvh];
+
+    bf16x8_t qop[8];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                             (static_cast<int64_t>(j) * p.hq + kvh * p.group + hh) * kD;
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+            const u32x4_t x = qrow_ok ? ld<u32x4_t>(qp + 16 * sd + 8 * g) : u32x4_t{0, 0, 0, 0};
+            qop[sd] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    float m = -INFINITY;
+    float l = 0.f;
+    f32x16_t acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+    const char* const kpool = static_cast<const char*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
+    const char* const vpool = static_cast<const char*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile * kElt;
+    const uint32_t koff = static_cast<uint32_t>(KV == PKV_BF16 ? 16 * t : ((t >> 4) * kD + (t & 15) * 8) * kElt);
+    const uint32_t voff = static_cast<uint32_t>(
+        KV == PKV_BF16 ? 16 * (64 * (t >> 6) + 16 * v_piece(t).g + v_piece(t).r) : byte_v_offset(t >> 1, (t & 1) * 8));
+    const uint32_t voff1 = static_cast<uint32_t>(KV == PKV_BF16 ? 0 : byte_v_offset(t >> 1, (t & 1) * 8 + 4));
+    const int krow0 = key_row(c32) * kKStride + 8 * g;
+    const int vrow0 = v_lds_offset(c32, g);
+
+    bool bad = false;
+    Stage<KV> sk, sv;  // every thread stages a piece of K and of V
+    auto stage_load = [&](int it) {
+        const char* kb[4];
+        const char* vb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int lb = min(it * 4 + b, nblk_seq - 1);
+            int32_t id = lb >= 0 ? trow[lb] : 0;
+            if (id < 0 || id >= p.num_blocks) {
+                bad = bad || lb >= 0;
+                id = 0;
+            }
+            kb[b] = kpool + id * blk_bytes;
+            vb[b] = vpool + id * blk_bytes;
+        }
+        sk.k_load(kb, koff);
+        sv.v_load(vb, voff, voff1);
+    };
+    auto stage_store = [&](int it, int buf) {
+        if ((it + 1) * kKeys > L) {
+            int valid[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) valid[b] = min(kBS, max(0, L - (it * 4 + b) * kBS));
+            sv.mask_tail(valid, t);
+        }
+        sk.k_store(ks[buf], t);
+        sv.v_store(vs[buf], t);
+    };
+
+    auto compute = [&](int it, int buf) {
+        const uint16_t* kc = ks[buf] + krow0;
+        const uint16_t* vc = vs[buf] + vrow0;
+        const int kbase = it * kKeys;
+        f32x16_t sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[kt][i] = 0.f;
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ld<u32x4_t>(kc + 32 * kt * kKStride + 16 * sd));
+                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[sd], sc[kt], 0, 0, 0);
+            }
+        }
+        if (kbase + kKeys - 1 > last_key) {  // the range's end inside this iteration
+            const int lastc = last_key - kbase - 8 * g;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kt + 16 * (i >> 3) + (i & 7) > lastc) sc[kt][i] = -INFINITY;
+        }
+        float mb = sc[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mb = fmaxf(mb, sc[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sc[1][i]);
+        mb *= scale;
+        if (__any(mb > m + kLazy)) {
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mn = fmaxf(m, mb);
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+            m = mn;
+        }
+        const float neg_m = m == -INFINITY ? 0.f : -m;
+        u32x4_t pw[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * h + 2 * e], scale, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * h + 2 * e + 1], scale, neg_m));
+                    const uint32_t w = pack_bf16(p0, p1);
+                    pw[kt][h][e] = w;
+                    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l, false);
+                }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, pw[kt][h]);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8_t a =
+                        __builtin_bit_cast(bf16x8_t, ld<u32x4_t>(vc + (2 * kt + h) * kTile + 32 * dt * kBS));
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+                }
+            }
+    };
+
+    // one register stage and two LDS buffers: the loads for iteration it + 1
+    // are issued before iteration it is computed and stored after it
+    const int it_begin = static_cast<int>(static_cast<int64_t>(n_iter) * part / p.parts);
+    const int it_end = static_cast<int>(static_cast<int64_t>(n_iter) * (part + 1) / p.parts);
+    const int last = max(it_end - 1, it_begin);
+    stage_load(it_begin);
+    if (it_end > it_begin) stage_store(it_begin, 0);
+    __syncthreads();
+    for (int it = it_begin; it < it_end; ++it) {
+        const int cur = (it - it_begin) & 1;
+        stage_load(min(it + 1, last));
+        compute(it, cur);
+        if (it + 1 < it_end) stage_store(it + 1, cur ^ 1);
+        __syncthreads();
+    }
+
+    bad = bad || !row_ok || (qrow_ok && broken[tok] != 0);
+    l += __shfl_xor(l, 32);
+    if (!qrow_ok) return;
+    const float nan = __builtin_nanf("");
+    float* sp = p.states + ((static_cast<int64_t>(part) * p.total_q + j) * p.hq + kvh * p.group + hh) * kState;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t v = {acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]};
+            st<f32x4_t>(sp + 32 * dt + 8 * q4 + 4 * g, bad ? f32x4_t{nan, nan, nan, nan} : v);
+        }
+    if (g == 0) st<float2>(sp + kD, float2{m, bad ? nan : l});
 }
 
 // Combines the key ranges of chunk queries q0 .. total_q - 1: for query q and
@@ -664,10 +865,13 @@ int env_int(const char* name) {
 }  // namespace
 
 // Key ranges the shared-prefix pass splits into: enough workgroups for one
-// per compute unit, each range at least one 64-key iteration, at most 8.
+// per compute unit (measured on 256 rows of a 2000-token prefix: two ranges
+// beat four, as each range's states are written and combined), each range at
+// least one 64-key iteration, at most 8.
 int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows) {
     const int32_t group = a->num_q_heads / c->num_kv_heads;
-    const int64_t tiles = static_cast<int64_t>((rows + kRows / group - 1) / (kRows / group)) * c->num_kv_heads;
+    const int64_t tiles =
+        static_cast<int64_t>((rows + kPrefixRows / group - 1) / (kPrefixRows / group)) * c->num_kv_heads;
     const int64_t iters = (static_cast<int64_t>(a->shared_prefix_blocks) * kBS + kKeys - 1) / kKeys;
     static const int env = env_int("PKV_PREFIX_PARTS");
     int64_t parts = env > 0 ? env : (device_cus() + tiles - 1) / tiles;
@@ -707,7 +911,7 @@ int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t row
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (c->kv_dtype == PKV_F32) return fail(PKV_ERR_UNSUPPORTED, "a shared prefix needs a bf16, fp8 or int8 cache");
     const int32_t group = a->num_q_heads / c->num_kv_heads;
-    const int32_t tile_tokens = kRows / group;
+    const int32_t tile_tokens = kPrefixRows / group;
     const int32_t q_tiles = (rows + tile_tokens - 1) / tile_tokens;
     const int64_t elt = c->kv_dtype == PKV_BF16 ? 2 : 1;
     const int64_t layer_elems = static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * kTile;
@@ -734,11 +938,11 @@ int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t row
     p.parts = prefix_parts(c, a, rows);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(q_tiles) * c->num_kv_heads * p.parts));
     if (c->kv_dtype == PKV_BF16)
-        hipLaunchKernelGGL((prefill_kernel<PKV_BF16, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefix_kernel<PKV_BF16>), grid, dim3(kPrefixThreads), 0, stream, p);
     else if (c->kv_dtype == PKV_FP8_E4M3)
-        hipLaunchKernelGGL((prefill_kernel<PKV_FP8_E4M3, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefix_kernel<PKV_FP8_E4M3>), grid, dim3(kPrefixThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<PKV_INT8, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prefix_kernel<PKV_INT8>), grid, dim3(kPrefixThreads), 0, stream, p);
     return PKV_OK;
 }
 
@@ -811,11 +1015,11 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     p.states = parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(a->workspace) + pre_off) : nullptr;
     const dim3 g1(static_cast<unsigned>(grid));
     if (c->kv_dtype == PKV_BF16)
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_BF16, false>), g1, dim3(pkv::kThreads), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_BF16>), g1, dim3(pkv::kThreads), 0, s, p);
     else if (c->kv_dtype == PKV_FP8_E4M3)
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_FP8_E4M3, false>), g1, dim3(pkv::kThreads), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_FP8_E4M3>), g1, dim3(pkv::kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_INT8, false>), g1, dim3(pkv::kThreads), 0, s, p);
+        hipLaunchKernelGGL((pkv::prefill_kernel<PKV_INT8>), g1, dim3(pkv::kThreads), 0, s, p);
     if (parts > 1) {
         // the chunk rows' queries are num_decode .. total_q - 1 (decode row i holds query i)
         const int64_t pairs = static_cast<int64_t>(a->total_q - a->num_decode) * a->num_q_heads;
