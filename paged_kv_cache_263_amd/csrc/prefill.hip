@@ -26,14 +26,18 @@
 // unit about as long as the products cost the matrix unit.
 //
 // Ping-pong.  The 8 waves form two groups of 4, one wave of each group per
-// SIMD.  Workgroup barriers cut the iterations into phases in which one group
-// issues matrix products (P.V of iteration i and K.Q^T of iteration i + 1)
-// while the other runs its softmax, and the groups swap at every barrier, so
-// the matrix and vector work of a SIMD overlap instead of following each
-// other.  Group 0 stages the K tiles and group 1 the V tiles, each in its
-// softmax phase, from registers loaded two phases earlier; two LDS buffers for
-// K and two for V are enough for this order (a buffer is rewritten only after
-// both groups have read it).  One staged tile serves 256 query rows.
+// SIMD.  Workgroup barriers cut the iterations into phases, and the groups
+// swap roles at every barrier.  In its matrix phase a wave computes the
+// exponentials of iteration i between the P.V products that consume them,
+// then K.Q^T of iteration i + 1; in its other phase it masks and takes the
+// maxima of those new scores (and, rarely, rescales) and stages the next K or
+// V tile.  The vector work of the exponentials runs in the shadow of the
+// wave's own products (measured faster than leaving the whole softmax to the
+// other phase), and the other group's short phase keeps the SIMD's second
+// wave off the matrix unit.  Group 0 stages the K tiles and group 1 the V
+// tiles, from registers loaded two phases earlier; two LDS buffers for K and
+// two for V are enough for this order (a buffer is rewritten only after both
+// groups have read it).  One staged tile serves 256 query rows.
 //
 // The lane holding a score column keeps that row's softmax state: running max
 // (rescaled lazily, only when a score passes it by 2^8) and normaliser.  The
@@ -56,6 +60,7 @@
 #include <cmath>
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -137,9 +142,10 @@ __device__ __forceinline__ VPiece v_piece(int u) {
 //
 // K (k_load, k_store): bf16 tiles (bf16_k_offset): piece u, token u % 16, d
 // 8 (u / 16) .. +7, so the group reads each 4 KiB tile contiguously.
-// One-byte tiles: row u / 16, codes (u % 16) * 8 .. +7, converted to bf16 on
-// load.  Tile addresses are uniform (one per block) and the thread's offset
-// inside a tile is fixed.
+// One-byte tiles: row u / 16, codes (u % 16) * 8 .. +7, held as codes in the
+// registers and converted to bf16 by the LDS store (so the conversion does not
+// wait for the load in the phase that issues it).  Tile addresses are uniform
+// (one per block) and the thread's offset inside a tile is fixed.
 template <int KV>
 struct Stage {
     u32x4_t k[4];
@@ -150,10 +156,14 @@ struct Stage {
                 k[b] = ld<u32x4_t>(kb[b] + koff);
             } else {
                 const u32x2_t kk = ld<u32x2_t>(kb[b] + koff);
-                const u32x2_t k0 = byte4_to_bf16x4<KV>(kk[0]), k1 = byte4_to_bf16x4<KV>(kk[1]);
-                k[b] = u32x4_t{k0[0], k0[1], k1[0], k1[1]};
+                k[b] = u32x4_t{kk[0], kk[1], 0u, 0u};
             }
         }
+    }
+    // 8 codes (two words) as 8 bf16 values
+    static __device__ __forceinline__ u32x4_t widen(uint32_t w0, uint32_t w1) {
+        const u32x2_t a = byte4_to_bf16x4<KV>(w0), b = byte4_to_bf16x4<KV>(w1);
+        return u32x4_t{a[0], a[1], b[0], b[1]};
     }
     __device__ __forceinline__ void k_store(uint16_t* ks, int u) const {
 #pragma unroll
@@ -161,7 +171,7 @@ struct Stage {
             if constexpr (KV == PKV_BF16)
                 st<u32x4_t>(ks + (b * kBS + (u & 15)) * kKStride + 8 * (u >> 4), k[b]);
             else
-                st<u32x4_t>(ks + (b * kBS + (u >> 4)) * kKStride + (u & 15) * 8, k[b]);
+                st<u32x4_t>(ks + (b * kBS + (u >> 4)) * kKStride + (u & 15) * 8, widen(k[b][0], k[b][1]));
         }
     }
 
@@ -173,13 +183,10 @@ struct Stage {
         u32x4_t* v = k;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if constexpr (KV == PKV_BF16) {
+            if constexpr (KV == PKV_BF16)
                 v[b] = ld<u32x4_t>(vb[b] + voff);
-            } else {
-                const u32x2_t vv = {ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1)};
-                const u32x2_t v0 = byte4_to_bf16x4<KV>(vv[0]), v1 = byte4_to_bf16x4<KV>(vv[1]);
-                v[b] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
-            }
+            else
+                v[b] = u32x4_t{ld<uint32_t>(vb[b] + voff), ld<uint32_t>(vb[b] + voff1), 0u, 0u};
         }
     }
     // Zero V of tokens at or past valid[b] (the row's partial last block and
@@ -192,9 +199,11 @@ struct Stage {
             uint32_t w[4] = {v[b][0], v[b][1], v[b][2], v[b][3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // token of element e
-                const int tok = KV == PKV_BF16 ? 4 * v_piece(u).g + (e & 3) : (u & 1) * 8 + e;
-                if (tok >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                if constexpr (KV == PKV_BF16) {  // bf16 element e: token 4 g + e % 4
+                    if (4 * v_piece(u).g + (e & 3) >= valid[b]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                } else {  // code byte e: token (u % 2) * 8 + e (a zero code is 0.0)
+                    if ((u & 1) * 8 + e >= valid[b]) w[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
+                }
             }
             v[b] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
@@ -211,7 +220,7 @@ struct Stage {
                 st<u32x2_t>(vt + v_lds_offset(d0, g >> 1), u32x2_t{v[b][0], v[b][1]});
                 st<u32x2_t>(vt + v_lds_offset(d0 + 16, g >> 1), u32x2_t{v[b][2], v[b][3]});
             } else {
-                st<u32x4_t>(vs + b * kTile + v_lds_offset(u >> 1, u & 1), v[b]);
+                st<u32x4_t>(vs + b * kTile + v_lds_offset(u >> 1, u & 1), widen(v[b][0], v[b][1]));
             }
         }
     }
@@ -351,28 +360,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     // keys are masked); a block id outside the pool reads block 0 and makes
     // the output NaN.
     bool bad = false;
-    auto tiles = [&](int it, const char* const pool, const char* tb[4]) {
+    // The block ids of an iteration are read from the table one staging step
+    // before its tiles are loaded (ids holds the next iteration's), so no
+    // phase waits out a table read before it can issue its tile loads.
+    int32_t ids[4];
+    auto load_ids = [&](int it) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) ids[b] = trow[min(it * 4 + b, nblk_seq - 1)];
+    };
+    auto tiles = [&](const char* const pool, const char* tb[4]) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int lb = min(it * 4 + b, nblk_seq - 1);
-            int32_t id = lb >= 0 ? trow[lb] : 0;
+            int32_t id = __builtin_amdgcn_readfirstlane(ids[b]);  // the same in every lane
             if (id < 0 || id >= p.num_blocks) {
-                bad = bad || lb >= 0;
+                bad = true;
                 id = 0;
             }
             tb[b] = pool + id * blk_bytes;
         }
     };
     Stage<KV> sr;
+    // load the tiles of iteration it (ids holds its block ids), then read the
+    // ids of iteration it + 1 (clamped to the row's blocks: in the table)
     auto k_load = [&](int it) {
         const char* kb[4];
-        tiles(it, kpool, kb);
+        tiles(kpool, kb);
         sr.k_load(kb, koff);
+        load_ids(it + 1);
     };
     auto v_load = [&](int it) {
         const char* vb[4];
-        tiles(it, vpool, vb);
+        tiles(vpool, vb);
         sr.v_load(vb, voff, voff1);
+        load_ids(it + 1);
     };
     auto k_store = [&](int it) { sr.k_store(ks[it & 1], u); };
     auto v_store = [&](int it) {
@@ -393,14 +413,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     // four products ahead of its use: in its matrix phase this wave is the
     // only one issuing products on its SIMD, so nothing else hides the LDS
     // latency.
-    auto prefetch4 = [] {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // four LDS reads
+    auto prefetch4 = [](auto products) {
+        constexpr int kAhead = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // four LDS reads
 #pragma unroll
-        for (int n = 0; n < 12; ++n) {
+        for (int n = 0; n < decltype(products)::value - kAhead; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the read four ahead
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     };
     // S^T = K . Q^T over the 64 keys of iteration it (K in buffer it & 1)
     auto qk = [&](int it) {
@@ -417,7 +438,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[sd], s[kt], 0, 0, 0);
             }
         }
-        prefetch4();
     };
     // O^T += V^T . P^T over iteration it's 64 keys (V in buffer it & 1)
     auto pv = [&](int it) {
@@ -434,9 +454,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
                     acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
                 }
             }
-        prefetch4();
     };
-    // Online softmax of iteration it's scores (in place in s) into pk.
+    // Online softmax of iteration it's scores (in place in s), in two parts
+    // that run in different phases.  smax: the causal mask, the maximum and
+    // the lazy rescale; sexp: the exponentials, their bf16 rounding into pk
+    // and the normaliser.  sexp runs in the wave's own matrix phase, between
+    // the P.V products that consume its results, so the vector unit works in
+    // the shadow of this wave's products while the other group's wave runs
+    // its (shorter) smax and staging.
     // Scores stay unscaled until the exponent (scale > 0, so the maximum
     // commutes with it); keys can pass a query's position only in the
     // iterations that reach the diagonal, so only those take the masked path
@@ -444,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     // four independent chains (one per 16-key step), so that one wave's
     // dependent instructions do not wait on each other.
     float lp[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's normaliser, per step
-    auto softmax = [&](int it) {
+    auto smax = [&](int it) {
         const int kbase = it * kKeys;
         if (kbase + kKeys - 1 > first_pos) {
             // score (kt, i) is key kbase + 8 g + c with c = 32 kt + 16 (i / 8) + i % 8
@@ -478,6 +503,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
             for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
             m = mn;
         }
+    };
+    auto sexp = [&] {
+        // The scores enter this phase here: a barrier does not order plain
+        // arithmetic, and the compiler would otherwise hoist part of the
+        // exponentials into the previous phase.
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) asm volatile("" : "+v"(s[kt]));
         const float neg_m = m == -INFINITY ? 0.f : -m;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -494,6 +526,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
                 }
             }
     };
+    // Every product of a matrix phase is issued before its barrier (the
+    // empty statements take the results as operands).
+    auto pin_s = [&] {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) asm volatile("" : "+v"(s[kt]));
+    };
+    auto pin_acc = [&] {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) asm volatile("" : "+v"(acc[dt]));
+    };
+    // A wave's matrix phase: P.V of iteration it, then K.Q^T of iteration
+    // it + 1 (next: there is one), with the operand reads four products ahead
+    // across both.
+    auto mma_phase = [&](int it, auto next) {
+        sexp();
+        pv(it);
+        if constexpr (decltype(next)::value) {
+            qk(it + 1);
+            prefetch4(std::integral_constant<int, 32>{});
+            pin_s();
+        } else {
+            prefetch4(std::integral_constant<int, 16>{});
+        }
+        pin_acc();
+    };
+    const std::true_type with_qk{};
+    const std::false_type last_pv{};
 
     // The workgroup's iterations: its key range of the tile's n_iter.
     const int ib = static_cast<int>(static_cast<int64_t>(n_iter) * part / p.parts);
@@ -501,17 +560,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     // Schedule (phases end at a barrier; group 0 = A, group 1 = B):
     //   prologue: A stages K(ib), K(ib+1) and loads K(ib+2); B stages V(ib) and loads V(ib+1)
     //   P0: A: qk(ib)
-    //   P1: A: softmax(ib)                           B: qk(ib)
+    //   P1: A: smax(ib)                                      B: qk(ib)
     //   for it = ib .. ie-1:
-    //     a: A: qk(it+1), pv(it)                       B: softmax(it), store V(it+1), load V(it+2)
-    //     b: A: softmax(it+1), store K(it+2), load K(it+3)   B: qk(it+1), pv(it)
-    // K(x) lands in ks[x & 1] in phase b of iteration x - 2, after both groups
-    // read K(x - 2) (B in phase b of iteration x - 3); V(x) lands in vs[x & 1]
-    // in phase a of iteration x - 1, after both read V(x - 2) (B in phase b of
-    // iteration x - 2).  Every wave passes the same barriers.
-    // Each group runs its own loop (straight code per phase for the
-    // compiler); both pass the same barriers.
+    //     a: A: sexp(it), pv(it), qk(it+1)                   B: smax(it), store V(it+1), load V(it+2)
+    //     b: A: smax(it+1), store K(it+2), load K(it+3)      B: sexp(it), pv(it), qk(it+1)
+    // (no qk(it+1) in the last iteration).  K(x) lands in ks[x & 1] in phase
+    // b of iteration x - 2, after both groups read K(x - 2) (B in phase b of
+    // iteration x - 3); V(x) lands in vs[x & 1] in phase a of iteration x - 1,
+    // after both read V(x - 2) (B in phase b of iteration x - 2).  Each group
+    // runs its own loop (straight code per phase for the compiler; the last
+    // iteration is peeled so the matrix phase has no branch); both pass the
+    // same barriers.
     if (ie > ib) {
+        load_ids(ib);
         if (grp == 0) {
             k_load(ib);
             k_store(ib);
@@ -523,19 +584,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
             lds_barrier();
             qk(ib);
             lds_barrier();
-            softmax(ib);
+            smax(ib);
             lds_barrier();
-            for (int it = ib; it < ie; ++it) {
-                if (it + 1 < ie) qk(it + 1);
-                pv(it);
+            for (int it = ib; it + 1 < ie; ++it) {
+                mma_phase(it, with_qk);
                 lds_barrier();
-                if (it + 1 < ie) softmax(it + 1);
+                smax(it + 1);
                 if (it + 2 < ie) {
                     k_store(it + 2);
                     if (it + 3 < ie) k_load(it + 3);
                 }
                 lds_barrier();
             }
+            mma_phase(ie - 1, last_pv);
+            lds_barrier();
+            lds_barrier();
         } else {
             v_load(ib);
             v_store(ib);
@@ -544,15 +607,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
             lds_barrier();
             qk(ib);
             lds_barrier();
-            for (int it = ib; it < ie; ++it) {
-                softmax(it);
-                if (it + 1 < ie) v_store(it + 1);
+            for (int it = ib; it + 1 < ie; ++it) {
+                smax(it);
+                v_store(it + 1);
                 if (it + 2 < ie) v_load(it + 2);
                 lds_barrier();
-                if (it + 1 < ie) qk(it + 1);
-                pv(it);
+                mma_phase(it, with_qk);
                 lds_barrier();
             }
+            smax(ie - 1);
+            lds_barrier();
+            mma_phase(ie - 1, last_pv);
+            lds_barrier();
         }
     }
 
@@ -683,15 +749,24 @@ __global__ __launch_bounds__(kPrefixThreads, 2) void prefix_kernel(const Prefill
 
     bool bad = false;
     Stage<KV> sk, sv;  // every thread stages a piece of K and of V
-    auto stage_load = [&](int it) {
+    // block ids read one staging step ahead of their tiles (as in the chunk
+    // kernel); ids holds those of the next stage_load
+    int32_t ids[4];
+    auto load_ids = [&](int it) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int lb = min(it * 4 + b, nblk_seq - 1);
+            ids[b] = lb >= 0 ? trow[lb] : 0;
+        }
+    };
+    auto stage_load = [&](int it, int next) {
         const char* kb[4];
         const char* vb[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int lb = min(it * 4 + b, nblk_seq - 1);
-            int32_t id = lb >= 0 ? trow[lb] : 0;
+            int32_t id = __builtin_amdgcn_readfirstlane(ids[b]);
             if (id < 0 || id >= p.num_blocks) {
-                bad = bad || lb >= 0;
+                bad = bad || nblk_seq > 0;  // (a row with no blocks reads block 0 unchecked)
                 id = 0;
             }
             kb[b] = kpool + id * blk_bytes;
@@ -699,6 +774,7 @@ __global__ __launch_bounds__(kPrefixThreads, 2) void prefix_kernel(const Prefill
         }
         sk.k_load(kb, koff);
         sv.v_load(vb, voff, voff1);
+        load_ids(next);
     };
     auto stage_store = [&](int it, int buf) {
         if ((it + 1) * kKeys > L) {
@@ -784,12 +860,13 @@ __global__ __launch_bounds__(kPrefixThreads, 2) void prefix_kernel(const Prefill
     const int it_begin = static_cast<int>(static_cast<int64_t>(n_iter) * part / p.parts);
     const int it_end = static_cast<int>(static_cast<int64_t>(n_iter) * (part + 1) / p.parts);
     const int last = max(it_end - 1, it_begin);
-    stage_load(it_begin);
+    load_ids(it_begin);
+    stage_load(it_begin, min(it_begin + 1, last));
     if (it_end > it_begin) stage_store(it_begin, 0);
     __syncthreads();
     for (int it = it_begin; it < it_end; ++it) {
         const int cur = (it - it_begin) & 1;
-        stage_load(min(it + 1, last));
+        stage_load(min(it + 1, last), min(it + 2, last));
         compute(it, cur);
         if (it + 1 < it_end) stage_store(it + 1, cur ^ 1);
         __syncthreads();
