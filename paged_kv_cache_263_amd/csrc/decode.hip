@@ -47,6 +47,7 @@
 // output.
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -78,6 +79,10 @@ struct DecodeParams {
     int32_t byte_kv;                // one-byte cache: V values carry v_scale
     int32_t rows, num_blocks, hkv, hq, group, max_blocks, max_kv_len, parts;  // parts = Q
     float scale_log2;               // log2(e) / sqrt(d)
+    // shared prefix: [rows][hq][kPrefixState] the suffix state of every row
+    // that one wavefront finished whole (acc[128] times v_scale, max,
+    // normaliser)
+    float* ws_rows;
 };
 
 // A buffer no wave of the kernel writes, read through the constant address
@@ -424,89 +429,6 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const DecodeParams p)
     }
 }
 
-// State of (row, head) qrow over the whole shared prefix from the states of
-// its key ranges: M = max m_i, l = sum l_i 2^(m_i - M), acc = sum acc_i
-// 2^(m_i - M), in range order.  This lane's 32 outputs (d = 16 n + 4 g + i)
-// go to acc; l is the lane group g = 0's share (0 for the others); returns M.
-// The loads are batched (all maxima at once, then two ranges at a time) so a
-// row's first piece waits for a few memory round trips, not two per range.
-constexpr int kMaxPrefixParts = 8;
-
-// The states of up to two key ranges, requested in one round before the
-// next tile's loads so that waiting for them waits for nothing else.
-struct PrefixLoads {
-    f32x4_t a0[8], a1[8];
-    float2 ml0, ml1;
-};
-__device__ __forceinline__ void prefix_request(const DecodeParams& p, int64_t qrow, int g, PrefixLoads& pl) {
-    const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
-    const float* s0 = p.ws_prefix + qrow * kPrefixState;
-    const float* s1 = p.prefix_parts > 1 ? s0 + stride : s0;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) pl.a0[n] = ld<f32x4_t>(s0 + 16 * n + 4 * g);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) pl.a1[n] = ld<f32x4_t>(s1 + 16 * n + 4 * g);
-    pl.ml0 = ld<float2>(s0 + kD);
-    pl.ml1 = ld<float2>(s1 + kD);
-}
-// The same combination as prefix_state, in the same order, from loaded states.
-__device__ __forceinline__ float prefix_combine(const DecodeParams& p, int g, const PrefixLoads& pl, f32x4_t acc[8],
-                                                float& l) {
-    const bool two = p.prefix_parts > 1;
-    const float mx = two ? fmaxf(pl.ml0.x, pl.ml1.x) : pl.ml0.x;
-    const float w0 = __builtin_amdgcn_exp2f(pl.ml0.x - mx);
-    float lsum = pl.ml0.y * w0;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = pl.a0[n] * w0;
-    if (two) {
-        const float w1 = __builtin_amdgcn_exp2f(pl.ml1.x - mx);
-        lsum += pl.ml1.y * w1;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] += pl.a1[n] * w1;
-    }
-    l = g == 0 ? lsum : 0.f;
-    return mx;
-}
-
-__device__ __forceinline__ float prefix_state(const DecodeParams& p, int64_t qrow, int g, f32x4_t acc[8], float& l) {
-    const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
-    const float* ps = p.ws_prefix + qrow * kPrefixState;
-    const int parts = p.prefix_parts;
-    float mk[kMaxPrefixParts];
-#pragma unroll
-    for (int k = 0; k < kMaxPrefixParts; ++k) mk[k] = k < parts ? ps[k * stride + kD] : -INFINITY;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMaxPrefixParts; ++k) mx = fmaxf(mx, mk[k]);
-    float lsum = 0.f;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < parts; k += 2) {
-        const bool two = k + 1 < parts;
-        const float* s0 = ps + k * stride;
-        const float* s1 = two ? s0 + stride : s0;
-        f32x4_t a0[8], a1[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) a0[n] = ld<f32x4_t>(s0 + 16 * n + 4 * g);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) a1[n] = ld<f32x4_t>(s1 + 16 * n + 4 * g);
-        const float2 ml0 = ld<float2>(s0 + kD);
-        const float2 ml1 = ld<float2>(s1 + kD);
-        const float w0 = __builtin_amdgcn_exp2f(ml0.x - mx);
-        lsum += ml0.y * w0;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] += a0[n] * w0;
-        if (two) {
-            const float w1 = __builtin_amdgcn_exp2f(ml1.x - mx);
-            lsum += ml1.y * w1;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) acc[n] += a1[n] * w1;
-        }
-    }
-    l = g == 0 ? lsum : 0.f;
-    return mx;
-}
-
 // Index of the row holding block position x: plan[b] <= x < plan[b+1]
 // (plan in LDS or in global memory).
 __device__ __forceinline__ int find_row(const int32_t* plan, int rows, int64_t x) {
@@ -588,7 +510,13 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
 // faster (Llama-shaped batch, 4 heads: 183 against 189 us); with eight heads
 // the extra reads cost more than they save (shared-prefix batch: 161 against
 // 155 us), and one-byte tiles are smaller still, so those keep the slots.
-template <int KV, bool LOCAL_PLAN, bool QMEM>
+//
+// PREFIX: the rows share their first prefix_blocks blocks, whose states the
+// shared-prefix pass computes (concurrently, on another stream, or before);
+// this kernel walks the blocks past the prefix only, and a row it finishes
+// whole goes to ws_rows as a state, not to the output: the merge kernel
+// combines it with the prefix states.
+template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
@@ -629,6 +557,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     const int u1 = range_start(U, wi + 1, Q);
     if (u0 >= u1) return;
     const bool head_ok = r < p.group;
+    const int skip = PREFIX ? p.prefix_blocks : 0;  // blocks of each row before the first one walked here
     const float nan = __builtin_nanf("");
     const f32x4_t nan4 = {nan, nan, nan, nan};
 
@@ -689,7 +618,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
             if constexpr (!QMEM) Tile<KV>::load_q(qn, q_ptr(bl), head_ok, g);  // requested before the tile, so waited for alone
             entered = true;
         }
-        const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + p.prefix_blocks + (x - lrb0)];
+        const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + skip + (x - lrb0)];
         const bool ok = id >= 0 && id < p.num_blocks;
         tbad = !ok;
         const int64_t off = static_cast<int64_t>(ok ? id : 0) * blk_stride;
@@ -737,26 +666,17 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
             c_len = l_len;
             cslot = lslot;
         }
-        // the row's first piece starts from its state over the shared prefix,
-        // the states of the prefix's key ranges combined (one lane group
-        // carries the normaliser); up to two ranges are requested before the
-        // next tile
-        const bool pstart = p.prefix_blocks > 0 && first && x == crb0;
-        const bool pfew = p.prefix_parts <= 2;
-        PrefixLoads pl;
-        if (pstart && pfew) prefix_request(p, qrow_of(bc), g, pl);
         QReg qm;
         if constexpr (QMEM) Tile<KV>::load_q(qm, q_ptr(bc), head_ok, g);
         issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
         if (first) {
             piece_end = crb1 < u1 ? crb1 : u1;
-            t1 = min(c_len, (p.prefix_blocks + static_cast<int>(piece_end - crb0)) * kBS);
+            t1 = min(c_len, (skip + static_cast<int>(piece_end - crb0)) * kBS);
             pbad = false;
             o = Online();
-            if (pstart) o.m = pfew ? prefix_combine(p, g, pl, o.acc, o.l) : prefix_state(p, qrow_of(bc), g, o.acc, o.l);
         }
         pbad = pbad || tb;
-        const int tok0 = (p.prefix_blocks + static_cast<int>(x - crb0)) * kBS;
+        const int tok0 = (skip + static_cast<int>(x - crb0)) * kBS;
         QReg q;
         if constexpr (QMEM) {
 #pragma unroll
@@ -772,7 +692,12 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
             const bool whole = crb0 >= u0 && crb1 <= u1;  // no other wavefront touches this row
             if (head_ok) {
                 const int64_t qrow = qrow_of(bc);
-                if (whole) {
+                if (whole && PREFIX) {
+                    float* sp = p.ws_rows + qrow * kPrefixState;
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) st<f32x4_t>(sp + 16 * n + 4 * g, pbad ? nan4 : o.acc[n] * vs);
+                    if (g == 0) st<float2>(sp + kD, float2{o.m, pbad ? nan : l});
+                } else if (whole) {
                     const float inv = pbad ? nan : vs / l;
 #pragma unroll
                     for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, qrow, 16 * n + 4 * g, o.acc[n] * inv);
@@ -819,6 +744,24 @@ __device__ __forceinline__ void store_out2(void* out, int64_t qrow, int d, float
     }
 }
 
+// The wavefronts whose ranges meet a row's blocks [rb0, rb1) of U: the row's
+// pieces come from wavefronts i0 .. i0 + n - 1.  Only the first can have
+// started its range in an earlier row (then this row is its second piece,
+// side0 = 1); every later one starts inside this row, so the row is its first
+// piece.
+__device__ __forceinline__ void row_pieces(const DecodeParams& p, int64_t U, int64_t rb0, int64_t rb1, int& i0, int& n,
+                                           int& side0) {
+    const int Q = effective_parts(U, p.parts);
+    i0 = static_cast<int>(rb0 * Q / U);
+    while (i0 + 1 < Q && range_start(U, i0 + 1, Q) <= rb0) ++i0;
+    while (i0 > 0 && range_start(U, i0, Q) > rb0) --i0;
+    int i1 = static_cast<int>((rb1 - 1) * Q / U);
+    while (i1 + 1 < Q && range_start(U, i1 + 1, Q) <= rb1 - 1) ++i1;
+    while (i1 > 0 && range_start(U, i1, Q) > rb1 - 1) --i1;
+    n = i1 - i0 + 1;
+    side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
+}
+
 template <int QT>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) {
     // kv head fastest, as in the decode kernel, so a head's partial results
@@ -835,46 +778,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
     const int64_t U = p.plan[p.rows];
     const int64_t rb0 = p.plan[b];
     const int64_t rb1 = p.plan[b + 1];
-    if (rb1 <= rb0) {
-        // no blocks past a shared prefix: the row's output is its prefix
-        // state, normalised (an invalid row got NaN with the plan)
-        if (p.prefix_blocks > 0 && row_valid(p.kv_lens[b], p)) {
-            const int64_t stride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
-            const float vs = p.byte_kv ? p.v_scale[kvh] : 1.f;
-            for (int hh = h0; hh < h0 + nh; ++hh) {
-                const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
-                float mx = -INFINITY;
-                for (int k = 0; k < p.prefix_parts; ++k) mx = fmaxf(mx, ps[k * stride + kD]);
-                float2 num = {0.f, 0.f};
-                float den = 0.f;
-                for (int k = 0; k < p.prefix_parts; ++k) {
-                    const float w = __builtin_amdgcn_exp2f(ps[k * stride + kD] - mx);
-                    const float2 a = ld<float2>(ps + k * stride + d);
-                    num.x += a.x * w;
-                    num.y += a.y * w;
-                    den += ps[k * stride + kD + 1] * w;
-                }
-                const float inv = vs / den;
-                store_out2<QT>(p.out, row_q + hh, d, num.x * inv, num.y * inv);
-            }
-        }
-        return;
-    }
-    if (U <= 0) return;
-    const int Q = effective_parts(U, p.parts);
-    // wavefronts whose ranges meet [rb0, rb1)
-    int i0 = static_cast<int>(rb0 * Q / U);
-    while (i0 + 1 < Q && range_start(U, i0 + 1, Q) <= rb0) ++i0;
-    while (i0 > 0 && range_start(U, i0, Q) > rb0) --i0;
-    int i1 = static_cast<int>((rb1 - 1) * Q / U);
-    while (i1 + 1 < Q && range_start(U, i1 + 1, Q) <= rb1 - 1) ++i1;
-    while (i1 > 0 && range_start(U, i1, Q) > rb1 - 1) --i1;
-    if (i0 == i1) return;  // written directly by the one wavefront
-    const int n = i1 - i0 + 1;
-    // Piece k comes from wavefront i0 + k.  Only the first can have started
-    // its range in an earlier row (then this row is its second piece, side 1);
-    // every later one starts inside this row, so the row is its first piece.
-    const int side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
+    if (rb1 <= rb0 || U <= 0) return;  // an invalid row (NaN from the plan)
+    int i0, n, side0;
+    row_pieces(p, U, rb0, rb1, i0, n, side0);
+    if (n == 1) return;  // written directly by the one wavefront
     const float* __restrict__ ws_ml = p.ws_ml;
     const float* __restrict__ ws_acc = p.ws_acc;
     const int64_t base0 = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp;
@@ -933,6 +840,121 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
 #undef PKV_MERGE_SLOT
 }
 
+// Shared prefix: the output of (row, query head) combines the states of the
+// prefix's key ranges (from the shared-prefix pass) with the row's suffix
+// pieces - its state in ws_rows when one wavefront finished the row, else the
+// divided pieces in the slots - by the max/normaliser algebra of the online
+// softmax, in that order.  The prefix states carry no v_scale, the suffix
+// states do.  A row with no block past the prefix is its prefix states alone.
+// Same grid and lanes as decode_merge_kernel (one wavefront per row, kv head
+// and group of kMergeHeads query heads, which measured faster than one per
+// query head).
+template <int QT>
+__global__ __launch_bounds__(64) void decode_merge_prefix_kernel(const DecodeParams p) {
+    const int hgroups = (p.group + kMergeHeads - 1) / kMergeHeads;
+    const int kvh = static_cast<int>(blockIdx.x % p.hkv);
+    const int rest = static_cast<int>(blockIdx.x / p.hkv);
+    const int h0 = (rest % hgroups) * kMergeHeads;
+    const int b = rest / hgroups;
+    const int d = 2 * threadIdx.x;
+    const int grp = p.group;
+    const int nh = min(kMergeHeads, grp - h0);
+    if (!row_valid(p.kv_lens[b], p)) return;  // NaN from the plan
+    const int64_t row_q = static_cast<int64_t>(b) * p.hq + kvh * grp;
+    const int64_t U = p.plan[p.rows];
+    const int64_t rb0 = p.plan[b];
+    const int64_t rb1 = p.plan[b + 1];
+    int i0 = 0, n = 0, side0 = 0;
+    if (rb1 > rb0) row_pieces(p, U, rb0, rb1, i0, n, side0);
+    const int64_t base0 = (static_cast<int64_t>(kvh) * p.parts + i0) * 2 * grp;
+    const int64_t pstride = static_cast<int64_t>(p.rows) * p.hq * kPrefixState;
+    const float vs = p.byte_kv ? p.v_scale[kvh] : 1.f;
+    const int parts = p.prefix_parts;
+    // slot of suffix piece k (n > 1) of head hh: wavefront i0 + k, side side0 for the first
+    auto slot = [&](int hh, int k) { return base0 + hh + (2 * k + (k == 0 ? side0 : 0)) * grp; };
+    if (parts <= 2 && n <= 2) {
+        // the usual case: every state of the wavefront's heads requested at
+        // once (indices past the last repeat it and are left out)
+        float2 ml[kMergeHeads][4], ac[kMergeHeads][4];  // prefix ranges 0, 1, suffix pieces 0, 1
+#pragma unroll
+        for (int a = 0; a < kMergeHeads; ++a) {
+            const int hh = h0 + min(a, nh - 1);
+            const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
+            const float* rs = p.ws_rows + (row_q + hh) * kPrefixState;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float* sk = ps + min(k, parts - 1) * pstride;
+                ml[a][k] = ld<float2>(sk + kD);
+                ac[a][k] = ld<float2>(sk + d);
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (n <= 1) {  // the whole-row state (read and left out when n == 0)
+                    ml[a][2 + k] = ld<float2>(rs + kD);
+                    ac[a][2 + k] = ld<float2>(rs + d);
+                } else {
+                    const int64_t sl = slot(hh, k);
+                    ml[a][2 + k] = ld<float2>(p.ws_ml + 2 * sl);
+                    ac[a][2 + k] = ld<float2>(p.ws_acc + sl * kD + d);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < kMergeHeads; ++a) {
+            if (a < nh) {
+                auto used = [&](int k) { return k < 2 ? k < parts : k - 2 < n; };
+                float mx = -INFINITY;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (used(k)) mx = fmaxf(mx, ml[a][k].x);
+                float2 num = {0.f, 0.f};
+                float den = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (used(k)) {
+                        const float w = __builtin_amdgcn_exp2f(ml[a][k].x - mx);
+                        const float wa = k < 2 ? w * vs : w;
+                        num.x += ac[a][k].x * wa;
+                        num.y += ac[a][k].y * wa;
+                        den += ml[a][k].y * w;
+                    }
+                }
+                store_out2<QT>(p.out, row_q + h0 + a, d, num.x / den, num.y / den);
+            }
+        }
+        return;
+    }
+    for (int hh = h0; hh < h0 + nh; ++hh) {
+        const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
+        const float* rs = p.ws_rows + (row_q + hh) * kPrefixState;
+        auto slot = [&](int k) { return base0 + hh + (2 * k + (k == 0 ? side0 : 0)) * grp; };
+        auto piece_ml = [&](int k) { return n == 1 ? ld<float2>(rs + kD) : ld<float2>(p.ws_ml + 2 * slot(k)); };
+        auto piece_acc = [&](int k) { return n == 1 ? ld<float2>(rs + d) : ld<float2>(p.ws_acc + slot(k) * kD + d); };
+        float mx = -INFINITY;
+        for (int k = 0; k < parts; ++k) mx = fmaxf(mx, ps[k * pstride + kD]);
+        for (int k = 0; k < n; ++k) mx = fmaxf(mx, piece_ml(k).x);
+        float2 num = {0.f, 0.f};
+        float den = 0.f;
+        for (int k = 0; k < parts; ++k) {
+            const float w = __builtin_amdgcn_exp2f(ps[k * pstride + kD] - mx);
+            const float2 a = ld<float2>(ps + k * pstride + d);
+            num.x += a.x * (w * vs);
+            num.y += a.y * (w * vs);
+            den += ps[k * pstride + kD + 1] * w;
+        }
+        for (int k = 0; k < n; ++k) {
+            const float2 ml = piece_ml(k);
+            const float w = __builtin_amdgcn_exp2f(ml.x - mx);
+            const float2 a = piece_acc(k);
+            num.x += a.x * w;
+            num.y += a.y * w;
+            den += ml.y * w;
+        }
+        store_out2<QT>(p.out, row_q + hh, d, num.x / den, num.y / den);
+    }
+}
+
 // Wavefronts per kv head, as a count per CU over all CUs: four (one per
 // SIMD) for bf16 caches, eight for the others.  These are the measured best
 // under streaming tile loads: bf16 decode of the Llama-shaped batch takes
@@ -958,25 +980,79 @@ int decode_parts_auto(int hkv, int kv_dtype) {
     return parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts);
 }
 
-template <bool LOCAL>
+template <bool LOCAL, bool PREFIX>
 void launch_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const DecodeParams& p) {
     switch (kv_dtype) {
-        case PKV_F32:
-            hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false>), grid, dim3(64), 0, stream, p);
+        case PKV_F32:  // (no shared prefix with an fp32 cache: refused before this)
+            if constexpr (!PREFIX) hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
             if (p.group <= 4)
-                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true>), grid, dim3(64), 0, stream, p);
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true, PREFIX>), grid, dim3(64), 0, stream, p);
             else
-                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false>), grid, dim3(64), 0, stream, p);
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_FP8_E4M3:
-            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL, false>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL, false>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
             break;
     }
+}
+
+// The shared-prefix pass runs on a stream of the library's, one per device,
+// forked from the caller's stream after the plan and joined back before the
+// merge with two events, so that it overlaps the decode kernel (the pass is
+// bound by the matrix cores, on cached prefix tiles; the decode kernel by HBM
+// streaming the suffixes).  Created on first use, with the device current,
+// and kept until the process ends.  The fork-join sequence of one call runs
+// under the device's lock, so concurrent calls from several host threads do
+// not interleave their event records.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+constexpr int kMaxSideDevices = 64;
+SideStream g_side[kMaxSideDevices];
+std::mutex g_side_init;
+
+// This device's side stream, or nullptr when the caller's stream belongs to
+// another device than the current one (then the pass runs on the caller's
+// stream, before the decode kernel).
+int side_stream(hipStream_t caller, SideStream** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (caller) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(caller, &sdev);
+        if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev) return PKV_OK;
+    }
+    if (dev < 0 || dev >= kMaxSideDevices) return PKV_OK;
+    SideStream& s = g_side[dev];
+    std::lock_guard<std::mutex> lock(g_side_init);
+    if (!s.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (j) (void)hipEventDestroy(j);
+            if (f) (void)hipEventDestroy(f);
+            if (st) (void)hipStreamDestroy(st);
+            return fail(PKV_ERR_HIP, "side stream for the shared-prefix pass: %s", hipGetErrorString(e));
+        }
+        s.fork = f;
+        s.join = j;
+        s.stream = st;
+    }
+    *out = &s;
+    return PKV_OK;
 }
 
 }  // namespace
@@ -992,17 +1068,21 @@ size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_
     const int64_t group = a->num_q_heads / c->num_kv_heads;
     const int64_t plan = (static_cast<int64_t>(rows) + 1 + 3) / 4 * 4;  // int32, 16-byte multiple
     const int64_t slots = static_cast<int64_t>(c->num_kv_heads) * Q * 2 * group;
-    const int64_t prefix = a->shared_prefix_blocks > 0
-                               ? static_cast<int64_t>(prefix_parts(c, a, rows)) * rows * a->num_q_heads * kPrefixState
-                               : 0;
+    // shared prefix: the states of its key ranges, then the rows' suffix states
+    const int64_t prefix = a->shared_prefix_blocks > 0 ? (static_cast<int64_t>(prefix_parts(c, a, rows)) + 1) * rows *
+                                                             a->num_q_heads * kPrefixState
+                                                       : 0;
     return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4 + prefix * 4);
 }
 
 // Launch decode over `rows` rows whose q/out/table/kv_lens start at the given
 // pointers (used by paged_attn_decode and by the decode rows of a prefill call).
+// With a shared prefix and fork_prefix, the shared-prefix pass runs on the
+// device's side stream, concurrently with the decode kernel; without
+// fork_prefix it runs first on `stream` (same kernels, same results).
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool fork_prefix) {
     auto mark = [&](int i) {
         if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
     };
@@ -1035,6 +1115,10 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.prefix_blocks = a->shared_prefix_blocks;
     p.prefix_parts = a->shared_prefix_blocks > 0 ? prefix_parts(c, a, rows) : 0;
     p.ws_prefix = a->shared_prefix_blocks > 0 ? p.ws_ml + slots * 2 : nullptr;
+    p.ws_rows = a->shared_prefix_blocks > 0
+                    ? const_cast<float*>(p.ws_prefix) + static_cast<int64_t>(p.prefix_parts) * rows * a->num_q_heads *
+                                                            kPrefixState
+                    : nullptr;
     p.byte_kv = is_byte_dtype(c->kv_dtype) ? 1 : 0;
     p.rows = rows;
     p.num_blocks = c->num_blocks;
@@ -1055,19 +1139,54 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
             hipLaunchKernelGGL(decode_plan_kernel<PKV_BF16>, dim3(1), dim3(1024), 0, stream, p);
     }
     mark(0);
-    if (p.prefix_blocks > 0) {
-        const int st = launch_prefix_states(c, a, rows, q, table, const_cast<float*>(p.ws_prefix), stream);
-        if (st) return st;
+    const bool prefix = p.prefix_blocks > 0;
+    SideStream* side = nullptr;
+    if (prefix) {
+        if (fork_prefix) {
+            const int st = side_stream(stream, &side);
+            if (st) return st;
+        }
+        float* states = const_cast<float*>(p.ws_prefix);
+        if (side) {
+            // The pass is queued first: queued second, its workgroups wait
+            // behind the decode kernel's persistent wavefronts and it ends
+            // long after them (measured 119 against 48 us on the 256-row
+            // shared-prefix batch).
+            std::lock_guard<std::mutex> lock(side->mu);
+            hipError_t e = hipEventRecord(side->fork, stream);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+            if (e != hipSuccess) return fail(PKV_ERR_HIP, "fork of the shared-prefix pass: %s", hipGetErrorString(e));
+            const int st = launch_prefix_states(c, a, rows, q, table, states, side->stream);
+            if (st) return st;
+            e = hipEventRecord(side->join, side->stream);
+            if (e != hipSuccess) return fail(PKV_ERR_HIP, "join of the shared-prefix pass: %s", hipGetErrorString(e));
+            // the join goes into the caller's stream after the decode kernel
+            // (below); until then this record is the one a wait sees
+            const dim3 g1(static_cast<unsigned>(grid));
+            local ? launch_decode_kernel<true, true>(c->kv_dtype, g1, stream, p)
+                  : launch_decode_kernel<false, true>(c->kv_dtype, g1, stream, p);
+            e = hipStreamWaitEvent(stream, side->join, 0);
+            if (e != hipSuccess) return fail(PKV_ERR_HIP, "join of the shared-prefix pass: %s", hipGetErrorString(e));
+        } else {
+            const int st = launch_prefix_states(c, a, rows, q, table, states, stream);
+            if (st) return st;
+        }
     }
-    const dim3 g1(static_cast<unsigned>(grid));
-    if (local)
-        launch_decode_kernel<true>(c->kv_dtype, g1, stream, p);
-    else
-        launch_decode_kernel<false>(c->kv_dtype, g1, stream, p);
-    mark(1);
+    if (!side) {
+        const dim3 g1(static_cast<unsigned>(grid));
+        if (local)
+            prefix ? launch_decode_kernel<true, true>(c->kv_dtype, g1, stream, p)
+                   : launch_decode_kernel<true, false>(c->kv_dtype, g1, stream, p);
+        else
+            prefix ? launch_decode_kernel<false, true>(c->kv_dtype, g1, stream, p)
+                   : launch_decode_kernel<false, false>(c->kv_dtype, g1, stream, p);
+    }
+    mark(1);  // (with a forked pass: after the later of the pass and the decode kernel)
     const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + kMergeHeads - 1) / kMergeHeads;
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads * hgroups));
-    if (f32)
+    if (prefix)  // (bf16 queries: a shared prefix needs a bf16 or one-byte cache)
+        hipLaunchKernelGGL(decode_merge_prefix_kernel<PKV_BF16>, mgrid, dim3(64), 0, stream, p);
+    else if (f32)
         hipLaunchKernelGGL(decode_merge_kernel<PKV_F32>, mgrid, dim3(64), 0, stream, p);
     else
         hipLaunchKernelGGL(decode_merge_kernel<PKV_BF16>, mgrid, dim3(64), 0, stream, p);
@@ -1103,7 +1222,7 @@ int paged_attn_decode(const pkv_cache* c, const pkv_attn_args* a, void* stream) 
     int st = pkv::check_attn(c, a);
     if (st) return st;
     return pkv::launch_decode(c, a, a->num_seqs, a->max_kv_len, a->q, a->out, a->block_table, a->kv_lens,
-                              a->workspace, a->workspace_bytes, static_cast<hipStream_t>(stream));
+                              a->workspace, a->workspace_bytes, static_cast<hipStream_t>(stream), true);
 }
 
 }  // extern "C"

@@ -69,7 +69,7 @@ namespace pkv {
 
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
-                  hipStream_t stream);
+                  hipStream_t stream, bool fork_prefix);
 
 namespace {
 
@@ -1051,7 +1051,7 @@ extern "C" int paged_attn_prefill_chunk(const pkv_cache* c, const pkv_attn_args*
     const int32_t dec_len = a->max_decode_kv_len > 0 ? a->max_decode_kv_len : a->max_kv_len;
     if (dec_len > a->max_kv_len) return fail(PKV_ERR_INVALID, "max_decode_kv_len exceeds max_kv_len");
     st = pkv::launch_decode(c, a, a->num_decode, dec_len, a->q, a->out, a->block_table, a->kv_lens,
-                            a->workspace, a->workspace_bytes, s);
+                            a->workspace, a->workspace_bytes, s, true);
     if (st) return st;
     if (n_pre == 0) {
         if (a->events[3]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[3]), s);
