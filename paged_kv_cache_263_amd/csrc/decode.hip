@@ -1039,8 +1039,12 @@ int side_stream(hipStream_t caller, SideStream** out) {
         hipStream_t st = nullptr;
         hipEvent_t f = nullptr, j = nullptr;
         e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        // device-scope events: the two streams are on one device, and a
+        // system-scope release would write the caches back at every record
+        // and hold the next kernel of that stream back
+        const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, flags);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, flags);
         if (e != hipSuccess) {
             if (j) (void)hipEventDestroy(j);
             if (f) (void)hipEventDestroy(f);
