@@ -47,11 +47,11 @@
 // output.
 #include <cmath>
 #include <cstdlib>
-#include <mutex>
 #include <type_traits>
 
 #include "device.h"
 #include "internal.h"
+#include "prefill_tiles.h"
 
 namespace pkv {
 namespace {
@@ -443,14 +443,14 @@ __device__ __forceinline__ int find_row(const int32_t* plan, int rows, int64_t x
 // Batches of at most kLocalPlanRows rows skip the plan kernel: every
 // wavefront computes the prefix sum of blocks per row itself, into LDS (one
 // coalesced load of 64 row lengths and one wave scan per 64 rows), and
-// workgroup 0 also stores it for the merge kernel and writes the NaN output
-// of invalid rows.  This takes one short kernel and its
+// the first wavefront (writer) also stores it for the merge kernel and writes
+// the NaN output of invalid rows.  This takes one short kernel and its
 // dependent global loads (a binary search through the global plan) off the
 // start of every wavefront.
 constexpr int kLocalPlanRows = 1024;
 
 template <int QT>
-__device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_sh, int lane) {
+__device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_sh, int lane, bool writer) {
     // Every row length is requested before the first is used (one memory
     // round trip, not one per 64 rows) and parked in this lane's own plan
     // slots, which the scan below overwrites in the same order.
@@ -485,10 +485,10 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
         }
         if (b < p.rows) {
             plan_sh[b + 1] = carry + v;
-            if (blockIdx.x == 0) p.plan[b + 1] = carry + v;
+            if (writer) p.plan[b + 1] = carry + v;
         }
         carry += __shfl(v, 63);
-        if (blockIdx.x == 0) {
+        if (writer) {
             uint64_t bad = __ballot(b < p.rows && invalid);
             while (bad) {
                 const int k = __builtin_ctzll(bad);
@@ -499,7 +499,7 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
     }
     if (lane == 0) {
         plan_sh[0] = 0;
-        if (blockIdx.x == 0) p.plan[0] = 0;
+        if (writer) p.plan[0] = 0;
     }
     __syncthreads();
 }
@@ -516,23 +516,35 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
 // this kernel walks the blocks past the prefix only, and a row it finishes
 // whole goes to ws_rows as a state, not to the output: the merge kernel
 // combines it with the prefix states.
+//
+// One wavefront of the decode grid: vblock is its index in the grid (one
+// wavefront per workgroup in decode_kernel; four per workgroup, after the
+// shared-prefix pass's workgroups, in prefix_decode_kernel), plan_sh and q_sh
+// its LDS (DecodeLds).
+template <int KV>
+struct DecodeLds {
+    using QReg = typename Tile<KV>::Q;
+    static constexpr int kQRegs = static_cast<int>(sizeof(QReg) / sizeof(QReg{}[0]));
+    static constexpr int kPlanInts = (kLocalPlanRows + 1 + 3) / 4 * 4;  // 16-byte multiple
+    static constexpr int kQSlots = 2 * kQRegs * 64;                     // u32x4_t
+    static constexpr int kBytes = kPlanInts * 4 + kQSlots * 16;
+};
 template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+__device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, int lane, int32_t* plan_sh,
+                                            u32x4_t* q_sh) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
-    __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
     using Elt = typename Tile<KV>::Elt;
     using QReg = typename Tile<KV>::Q;
-    constexpr int kQRegs = static_cast<int>(sizeof(QReg) / sizeof(QReg{}[0]));
-    const int lane = threadIdx.x;
+    constexpr int kQRegs = DecodeLds<KV>::kQRegs;
     const int r = lane & 15;
     const int g = lane >> 4;
     // kv head fastest: consecutive workgroups are dealt round-robin to the 8
     // XCDs, so with 8 kv heads each XCD streams one head (and keeps that
     // head's shared-prefix blocks in its own L2).
-    const int kvh = blockIdx.x % p.hkv;
-    const int wi = blockIdx.x / p.hkv;
-    if constexpr (LOCAL_PLAN) local_plan<QT>(p, plan_sh, lane);
+    const int kvh = vblock % p.hkv;
+    const int wi = vblock / p.hkv;
+    if constexpr (LOCAL_PLAN) local_plan<QT>(p, plan_sh, lane, vblock == 0);
     // The plan, the row lengths and the block table are read wave-uniformly:
     // the plan from LDS (or, when the plan kernel wrote it, through the
     // constant address space) and the other two through the constant address
@@ -593,7 +605,6 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     // cursor reads its row's slot at every block.  Kept out of loop-carried
     // registers, a query load is never waited for at the loop's back edge
     // (a register copy there would also wait for the tile in flight).
-    __shared__ u32x4_t q_sh[2 * kQRegs * 64];
     auto q_store = [&](int slot, const QReg& v) {
 #pragma unroll
         for (int i = 0; i < kQRegs; ++i) q_sh[(slot * kQRegs + i) * 64 + lane] = __builtin_bit_cast(u32x4_t, v[i]);
@@ -719,6 +730,39 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         if (x + 1 >= u1) break;
         step(t[1], tbad[1], t[0], tbad[0], x + 1);
     }
+}
+
+template <int KV, bool LOCAL_PLAN, bool QMEM>
+__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+    __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
+    __shared__ u32x4_t q_sh[DecodeLds<KV>::kQSlots];
+    decode_wave<KV, LOCAL_PLAN, QMEM, false>(p, blockIdx.x, threadIdx.x, plan_sh, q_sh);
+}
+
+// A decode call with a shared prefix, in one launch: workgroups 0 ..
+// n_prefix - 1 run the shared-prefix pass (prefix_tile, 4 waves each), the
+// rest run the decode wavefronts over the suffixes, four per workgroup.  The
+// pass's workgroups are dispatched first and the two kinds share the compute
+// units (two workgroups per CU: one of each while the pass lasts), so the pass
+// (matrix cores, on cached prefix tiles) runs under the decode's HBM
+// streaming.  Both carve one LDS allocation.
+constexpr int kFusedThreads = 256;
+static_assert(kFusedThreads == pf::kPrefixThreads, "one workgroup size for both roles");
+constexpr int kFusedLds = pf::kPrefixLdsBytes;
+template <int KV, bool LOCAL_PLAN, bool QMEM>
+__global__ __launch_bounds__(kFusedThreads, 2) void prefix_decode_kernel(const DecodeParams p, const pf::PrefillParams pp,
+                                                                         int n_prefix) {
+    static_assert(4 * DecodeLds<KV>::kBytes <= kFusedLds, "four decode wavefronts fit the pass's LDS");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kFusedLds];
+    if (static_cast<int>(blockIdx.x) < n_prefix) {
+        pf::prefix_tile<KV>(pp, blockIdx.x, lds);
+        return;
+    }
+    const int w = threadIdx.x >> 6;
+    unsigned char* mine = lds + w * DecodeLds<KV>::kBytes;
+    decode_wave<KV, LOCAL_PLAN, QMEM, true>(p, (blockIdx.x - n_prefix) * 4 + w, threadIdx.x & 63,
+                                            reinterpret_cast<int32_t*>(mine),
+                                            reinterpret_cast<u32x4_t*>(mine + DecodeLds<KV>::kPlanInts * 4));
 }
 
 // Merge the pieces of one (row, query head) that was divided between
@@ -980,83 +1024,50 @@ int decode_parts_auto(int hkv, int kv_dtype) {
     return parts < 1 ? 1 : (parts > kMaxParts ? kMaxParts : parts);
 }
 
-template <bool LOCAL, bool PREFIX>
+template <bool LOCAL>
 void launch_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const DecodeParams& p) {
     switch (kv_dtype) {
-        case PKV_F32:  // (no shared prefix with an fp32 cache: refused before this)
-            if constexpr (!PREFIX) hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false, false>), grid, dim3(64), 0, stream, p);
+        case PKV_F32:
+            hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
             if (p.group <= 4)
-                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true, PREFIX>), grid, dim3(64), 0, stream, p);
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true>), grid, dim3(64), 0, stream, p);
             else
-                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
+                hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_FP8_E4M3:
-            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_FP8_E4M3, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         default:
-            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL, false, PREFIX>), grid, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<PKV_INT8, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
     }
 }
 
-// The shared-prefix pass runs on a stream of the library's, one per device,
-// forked from the caller's stream after the plan and joined back before the
-// merge with two events, so that it overlaps the decode kernel (the pass is
-// bound by the matrix cores, on cached prefix tiles; the decode kernel by HBM
-// streaming the suffixes).  Created on first use, with the device current,
-// and kept until the process ends.  The fork-join sequence of one call runs
-// under the device's lock, so concurrent calls from several host threads do
-// not interleave their event records.
-struct SideStream {
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    std::mutex mu;
-};
-constexpr int kMaxSideDevices = 64;
-SideStream g_side[kMaxSideDevices];
-std::mutex g_side_init;
-
-// This device's side stream, or nullptr when the caller's stream belongs to
-// another device than the current one (then the pass runs on the caller's
-// stream, before the decode kernel).
-int side_stream(hipStream_t caller, SideStream** out) {
-    *out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (caller) {
-        hipDevice_t sdev = 0;
-        e = hipStreamGetDevice(caller, &sdev);
-        if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
-        if (sdev != dev) return PKV_OK;
+// (no shared prefix with an fp32 cache: refused by the argument checks)
+template <bool LOCAL>
+void launch_prefix_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const DecodeParams& p,
+                                 const pf::PrefillParams& pp, int n_prefix) {
+    const dim3 block(kFusedThreads);
+    switch (kv_dtype) {
+        case PKV_BF16:
+            if (p.group <= 4)
+                hipLaunchKernelGGL((prefix_decode_kernel<PKV_BF16, LOCAL, true>), grid, block, 0, stream, p, pp,
+                                   n_prefix);
+            else
+                hipLaunchKernelGGL((prefix_decode_kernel<PKV_BF16, LOCAL, false>), grid, block, 0, stream, p, pp,
+                                   n_prefix);
+            break;
+        case PKV_FP8_E4M3:
+            hipLaunchKernelGGL((prefix_decode_kernel<PKV_FP8_E4M3, LOCAL, false>), grid, block, 0, stream, p, pp,
+                               n_prefix);
+            break;
+        default:
+            hipLaunchKernelGGL((prefix_decode_kernel<PKV_INT8, LOCAL, false>), grid, block, 0, stream, p, pp,
+                               n_prefix);
+            break;
     }
-    if (dev < 0 || dev >= kMaxSideDevices) return PKV_OK;
-    SideStream& s = g_side[dev];
-    std::lock_guard<std::mutex> lock(g_side_init);
-    if (!s.stream) {
-        hipStream_t st = nullptr;
-        hipEvent_t f = nullptr, j = nullptr;
-        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-        // device-scope events: the two streams are on one device, and a
-        // system-scope release would write the caches back at every record
-        // and hold the next kernel of that stream back
-        const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, flags);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, flags);
-        if (e != hipSuccess) {
-            if (j) (void)hipEventDestroy(j);
-            if (f) (void)hipEventDestroy(f);
-            if (st) (void)hipStreamDestroy(st);
-            return fail(PKV_ERR_HIP, "side stream for the shared-prefix pass: %s", hipGetErrorString(e));
-        }
-        s.fork = f;
-        s.join = j;
-        s.stream = st;
-    }
-    *out = &s;
-    return PKV_OK;
 }
 
 }  // namespace
@@ -1081,12 +1092,9 @@ size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_
 
 // Launch decode over `rows` rows whose q/out/table/kv_lens start at the given
 // pointers (used by paged_attn_decode and by the decode rows of a prefill call).
-// With a shared prefix and fork_prefix, the shared-prefix pass runs on the
-// device's side stream, concurrently with the decode kernel; without
-// fork_prefix it runs first on `stream` (same kernels, same results).
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
-                  hipStream_t stream, bool fork_prefix) {
+                  hipStream_t stream) {
     auto mark = [&](int i) {
         if (a->events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a->events[i]), stream);
     };
@@ -1144,48 +1152,22 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     }
     mark(0);
     const bool prefix = p.prefix_blocks > 0;
-    SideStream* side = nullptr;
     if (prefix) {
-        if (fork_prefix) {
-            const int st = side_stream(stream, &side);
-            if (st) return st;
-        }
-        float* states = const_cast<float*>(p.ws_prefix);
-        if (side) {
-            // The pass is queued first: queued second, its workgroups wait
-            // behind the decode kernel's persistent wavefronts and it ends
-            // long after them (measured 119 against 48 us on the 256-row
-            // shared-prefix batch).
-            std::lock_guard<std::mutex> lock(side->mu);
-            hipError_t e = hipEventRecord(side->fork, stream);
-            if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-            if (e != hipSuccess) return fail(PKV_ERR_HIP, "fork of the shared-prefix pass: %s", hipGetErrorString(e));
-            const int st = launch_prefix_states(c, a, rows, q, table, states, side->stream);
-            if (st) return st;
-            e = hipEventRecord(side->join, side->stream);
-            if (e != hipSuccess) return fail(PKV_ERR_HIP, "join of the shared-prefix pass: %s", hipGetErrorString(e));
-            // the join goes into the caller's stream after the decode kernel
-            // (below); until then this record is the one a wait sees
-            const dim3 g1(static_cast<unsigned>(grid));
-            local ? launch_decode_kernel<true, true>(c->kv_dtype, g1, stream, p)
-                  : launch_decode_kernel<false, true>(c->kv_dtype, g1, stream, p);
-            e = hipStreamWaitEvent(stream, side->join, 0);
-            if (e != hipSuccess) return fail(PKV_ERR_HIP, "join of the shared-prefix pass: %s", hipGetErrorString(e));
-        } else {
-            const int st = launch_prefix_states(c, a, rows, q, table, states, stream);
-            if (st) return st;
-        }
-    }
-    if (!side) {
+        pf::PrefillParams pp;
+        const int n_prefix = prefix_pass_params(c, a, rows, q, table, const_cast<float*>(p.ws_prefix), &pp);
+        const dim3 g(static_cast<unsigned>(n_prefix + (grid + 3) / 4));
+        if (local)
+            launch_prefix_decode_kernel<true>(c->kv_dtype, g, stream, p, pp, n_prefix);
+        else
+            launch_prefix_decode_kernel<false>(c->kv_dtype, g, stream, p, pp, n_prefix);
+    } else {
         const dim3 g1(static_cast<unsigned>(grid));
         if (local)
-            prefix ? launch_decode_kernel<true, true>(c->kv_dtype, g1, stream, p)
-                   : launch_decode_kernel<true, false>(c->kv_dtype, g1, stream, p);
+            launch_decode_kernel<true>(c->kv_dtype, g1, stream, p);
         else
-            prefix ? launch_decode_kernel<false, true>(c->kv_dtype, g1, stream, p)
-                   : launch_decode_kernel<false, false>(c->kv_dtype, g1, stream, p);
+            launch_decode_kernel<false>(c->kv_dtype, g1, stream, p);
     }
-    mark(1);  // (with a forked pass: after the later of the pass and the decode kernel)
+    mark(1);
     const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + kMergeHeads - 1) / kMergeHeads;
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads * hgroups));
     if (prefix)  // (bf16 queries: a shared prefix needs a bf16 or one-byte cache)
@@ -1226,7 +1208,7 @@ int paged_attn_decode(const pkv_cache* c, const pkv_attn_args* a, void* stream) 
     int st = pkv::check_attn(c, a);
     if (st) return st;
     return pkv::launch_decode(c, a, a->num_seqs, a->max_kv_len, a->q, a->out, a->block_table, a->kv_lens,
-                              a->workspace, a->workspace_bytes, static_cast<hipStream_t>(stream), true);
+                              a->workspace, a->workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -29,7 +29,5 @@ int prefix_parts(const pkv_cache* c, const pkv_attn_args* a, int32_t rows);
 // Workspace of a prefill call's chunk rows (their key-range states; 0 when the
 // tiles are not split), placed after the decode rows' part, 256-byte aligned.
 size_t prefill_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a);
-int launch_prefix_states(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, const void* q,
-                         const int32_t* table, float* states, void* stream);
 
 }  // namespace pkv

@@ -32,7 +32,7 @@ namespace pkv {
 
 int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int32_t max_kv_len, const void* q,
                   void* out, const int32_t* table, const int32_t* kv_lens, void* workspace, size_t ws_bytes,
-                  hipStream_t stream, bool fork_prefix);
+                  hipStream_t stream);
 
 namespace {
 
@@ -90,5 +90,5 @@ extern "C" int paged_attn_decode_noalloc(const pkv_cache* c, const pkv_attn_args
         if (st) return st;
     }
     return pkv::launch_decode(c, a, a->num_seqs, a->max_kv_len, a->q, a->out, a->block_table, a->kv_lens, ptr,
-                              pkv::kScratchBytes, s, false);
+                              pkv::kScratchBytes, s);
 }
