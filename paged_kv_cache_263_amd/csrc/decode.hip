@@ -45,6 +45,11 @@
 // on the lengths only, so every sum is taken in an order fixed by logical
 // positions and a permutation of the physical blocks changes no bit of the
 // output.
+//
+// Shared prefix.  When every row's table starts with the same blocks, one
+// launch (prefix_decode_kernel) runs the shared-prefix pass over those blocks
+// (prefix_tile, prefill_tiles.h) in the same grid as the decode wavefronts
+// over the rest, and decode_merge_prefix_kernel combines the two.
 #include <cmath>
 #include <cstdlib>
 #include <type_traits>

@@ -55,8 +55,10 @@
 // keys are split into ranges (whole iterations); a range's state (unnormalised
 // output, running max, normaliser) goes to the workspace and a merge kernel
 // combines the ranges of every query with the max/normaliser algebra of the
-// online softmax.  The same mode, without the causal mask, computes the decode
-// rows' states over a prefix all rows share (the shared-prefix pass).
+// online softmax.  The same products and softmax, without the causal mask,
+// compute the decode rows' states over a prefix all rows share (the
+// shared-prefix pass: prefix_tile in prefill_tiles.h, which the decode launch
+// runs).
 #include <cmath>
 
 #include <cstdlib>
