@@ -77,11 +77,11 @@ def test_chunked_1024_over_16k_context_with_32_decodes(kv, parts):
     check_prefill(chunked_workload(16384, kv), tokens=CHUNK_TOKENS, parts=parts)
 
 
-@pytest.mark.parametrize("chunk,hq", [(512, 64), (1024, 32)])
+@pytest.mark.parametrize("chunk,hq", [(512, 64), (1024, 32), (512, 32)])
 def test_chunk_split_over_key_ranges_at_64k(chunk, hq):
     """Launches with fewer query tiles than compute units (a 512-query chunk
-    at eight heads per kv head, or a 1024-query chunk at four) split every
-    tile's 64K context into key ranges and merge them."""
+    at eight or four heads per kv head, or a 1024-query chunk at four) split
+    every tile's 64K context into key ranges and merge them."""
     w = W.chunked(context=65536, chunk=chunk, hq=hq)
     w.variant = "peaked"
     check_prefill(w, tokens=[t for t in CHUNK_TOKENS if t < chunk])

@@ -1,14 +1,15 @@
 """GPU checks of swapping blocks to pinned host memory and back (through the
 C ABI): the host copy holds each block's bytes in the documented slot layout,
 and a sequence swapped out, its blocks reused by another sequence, then swapped
-back into different blocks decodes to the same bits as before."""
+back into different blocks decodes to the same bits as before, which match the
+oracle within the cache dtype's tolerance."""
 
 import numpy as np
 import pytest
 import torch
 
 import workloads as W
-from harness import HipSide
+from harness import TOL, HipSide, OracleSide, compare
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
@@ -26,6 +27,9 @@ def test_swap_round_trip_is_bit_exact(kv, layers):
     hip = HipSide(w, layer=layers - 1, num_layers=layers)
     before = hip.decode().clone()
     row = 1
+    torch.cuda.synchronize()
+    compare(before[[row]].float().cpu().numpy(), np.stack([OracleSide(w).decode(row)]), TOL[kv],
+            f"swap kv={kv}: row {row} before the swap")
     seq = w.batch[row]
     ids = pk.seq_swap_out(hip.pool, seq)
     assert len(ids) == -(-700 // 16)
