@@ -462,6 +462,28 @@ def test_shared_prefix_pass_rows_without_suffix():
     assert torch.isnan(out[3].float()).all() and torch.isfinite(out[2].float()).all()
 
 
+@pytest.mark.parametrize("hq", [16, 8])
+def test_shared_prefix_pass_beyond_the_in_kernel_plan(hq):
+    """More than 1024 rows under the shared-prefix promise: the plan kernel
+    writes the plan that the one launch (prefix pass + suffix decode) reads,
+    for eight and four query heads per kv head (the two bf16 decode forms);
+    sampled rows on both sides of the 1024-row mark match the oracle, and the
+    output equals the no-allocation entry point's bit for bit."""
+    import paged_kv_cache_263_amd as pk
+
+    rows = 1100
+    w = W.shared_prefix(nseq=rows, prefix=256, min_suffix=2, max_suffix=120, hq=hq, hkv=2, variant="peaked")
+    hip = HipSide(w)
+    case(f"shared prefix over {rows} rows, hq={hq}")
+    sample = [0, 1, 511, 1023, 1024, 1025, rows - 2, rows - 1]
+    _, out = check_decode(w, rows=sample, hip=hip, shared_prefix_blocks=16)
+    again = torch.full_like(out, float("nan"))
+    pk.paged_attn_decode_noalloc(hip.cache, hip.q, hip.table, hip.kv_lens, hip.max_kv_len, again,
+                                 shared_prefix_blocks=16)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
+
+
 def test_shared_prefix_pass_placement_invariance():
     w = W.shared_prefix(nseq=32, max_suffix=300, hq=32, hkv=8, variant="needle")
     case("shared prefix: placement invariance")
