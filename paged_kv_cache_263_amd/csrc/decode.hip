@@ -511,10 +511,13 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
 
 // QMEM: the query operand is read from memory at every block (the row's
 // query rows stay in the caches) instead of from its LDS slot.  Chosen for
-// bf16 caches with at most four query heads per kv head, where it measured
-// faster (Llama-shaped batch, 4 heads: 183 against 189 us); with eight heads
-// the extra reads cost more than they save (shared-prefix batch: 161 against
-// 155 us), and one-byte tiles are smaller still, so those keep the slots.
+// bf16 caches with at most eight query heads per kv head, where it measured
+// faster (Llama-shaped batch, 4 heads: 183 against 189 us; the same lengths
+// with 8 heads: 192.0 against 196.8 us per call, and the chunked call's 32
+// decode rows 95.8 against 97.4 us).  The shared-prefix launch keeps the
+// slots above four heads: there the extra reads meet the prefix pass's in the
+// same grid (133 against 145 us).  One-byte tiles are smaller still, so those
+// keep the slots.
 //
 // PREFIX: the rows share their first prefix_blocks blocks, whose states the
 // shared-prefix pass computes (concurrently, on another stream, or before);
@@ -1036,7 +1039,7 @@ void launch_decode_kernel(int kv_dtype, dim3 grid, hipStream_t stream, const Dec
             hipLaunchKernelGGL((decode_kernel<PKV_F32, LOCAL, false>), grid, dim3(64), 0, stream, p);
             break;
         case PKV_BF16:
-            if (p.group <= 4)
+            if (p.group <= 8)
                 hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, true>), grid, dim3(64), 0, stream, p);
             else
                 hipLaunchKernelGGL((decode_kernel<PKV_BF16, LOCAL, false>), grid, dim3(64), 0, stream, p);
