@@ -280,10 +280,10 @@ typedef struct {
     size_t workspace_bytes;
     /* optional profiling: hipEvent_t handles (NULL entries are skipped) that
      * the call records on its stream: [0] just before the decode kernel (after
-     * the plan kernel that batches of more than 1024 rows need; before the
-     * shared-prefix pass, if any), [1] after the decode kernel, [2] after the
-     * decode merge kernel, [3] after the prefill kernel.  The caller owns the
-     * events. */
+     * the plan kernel that batches of more than 1024 rows need; with a shared
+     * prefix, before the one launch that runs the shared-prefix pass and the
+     * decode), [1] after it, [2] after the decode merge kernel, [3] after the
+     * prefill kernel.  The caller owns the events. */
     void* events[4];
 } pkv_attn_args;
 
@@ -303,12 +303,13 @@ int paged_attn_workspace_size(const pkv_cache* cache, const pkv_attn_args* args,
  * block id gets NaN output. */
 /* With shared_prefix_blocks = S > 0 (the rows' tables all start with the same
  * S block ids: a shared prefix, [P2] "Sharing, and what makes a prefix
- * reusable"), the call first computes, on the matrix cores, every row's
- * attention state (running max, normaliser, unnormalised output) over the
- * 16 S prefix tokens, reading those blocks once per kv head instead of once per
- * row, then runs the decode over each row's remaining blocks starting from
- * that state.  The result is the same attention (a different summation
- * order); it is still independent of where the blocks sit. */
+ * reusable"), the call computes, on the matrix cores, every row's attention
+ * state (running max, normaliser, unnormalised output) over the 16 S prefix
+ * tokens, reading those blocks once per kv head instead of once per row, in
+ * the same launch as the decode over each row's remaining blocks; the merge
+ * kernel combines the two states.  The result is the same attention (a
+ * different summation order); it is still independent of where the blocks
+ * sit. */
 int paged_attn_decode(const pkv_cache* cache, const pkv_attn_args* args, void* stream);
 
 /* paged_attn_decode for callers that cannot allocate device memory (code
