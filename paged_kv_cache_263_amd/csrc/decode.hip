@@ -524,19 +524,18 @@ __device__ __forceinline__ void local_plan(const DecodeParams& p, int32_t* plan_
 // this kernel walks the blocks past the prefix only, and a row it finishes
 // whole goes to ws_rows as a state, not to the output: the merge kernel
 // combines it with the prefix states.
-//
-// One wavefront of the decode grid: vblock is its index in the grid (one
-// wavefront per workgroup in decode_kernel; four per workgroup, after the
-// shared-prefix pass's workgroups, in prefix_decode_kernel), plan_sh and q_sh
-// its LDS (DecodeLds).
 template <int KV>
-struct DecodeLds {
+struct DecodeLds {  // LDS of one decode wavefront: its plan (if it builds one) and its two query slots
     using QReg = typename Tile<KV>::Q;
     static constexpr int kQRegs = static_cast<int>(sizeof(QReg) / sizeof(QReg{}[0]));
     static constexpr int kPlanInts = (kLocalPlanRows + 1 + 3) / 4 * 4;  // 16-byte multiple
     static constexpr int kQSlots = 2 * kQRegs * 64;                     // u32x4_t
     static constexpr int kBytes = kPlanInts * 4 + kQSlots * 16;
 };
+// One wavefront of the decode grid: vblock is its index in the grid (one
+// wavefront per workgroup in decode_kernel; four per workgroup, after the
+// shared-prefix pass's workgroups, in prefix_decode_kernel), plan_sh and q_sh
+// its LDS.
 template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, int lane, int32_t* plan_sh,
                                             u32x4_t* q_sh) {
