@@ -783,8 +783,13 @@ constexpr int kMergeBatch = 8;
 // owns d = 2 l, 2 l + 1 of those heads.  The row's plan and wavefront range
 // are worked out once; then every load of a batch is issued together, so a
 // row cut into at most kMergeBatch pieces costs one round of loads after the
-// plan's.
-constexpr int kMergeHeads = 4;
+// plan's.  One head per wavefront measured fastest (Llama-shaped batch 4.7
+// against 7.2 us with four heads, whose 64 wave-uniform piece addresses per
+// batch spilled scalar registers; fp8 long context 7.5 against 16.6 us); the
+// shared-prefix merge, with few pieces per row, is fastest at four
+// (kPrefixMergeHeads: 10.2 against 15.5 us at one).
+constexpr int kMergeHeads = 1;
+constexpr int kPrefixMergeHeads = 4;
 
 template <int QT>
 __device__ __forceinline__ void store_out2(void* out, int64_t qrow, int d, float a, float b) {
@@ -795,22 +800,37 @@ __device__ __forceinline__ void store_out2(void* out, int64_t qrow, int d, float
     }
 }
 
+// Range bounds for the merge kernels: floor(U i / Q), equal to range_start,
+// in 32-bit arithmetic (the 64-bit division's inlined code made up most of a
+// merge kernel's instructions).  With U = a Q + b (0 <= b < Q), U i / Q =
+// a i + b i / Q, where a i <= U < 2^31 and b i < Q^2 <= 2^24 (Q <= 4096, the
+// decode's partition limit, checked on the host).
+struct RangeBounds {
+    int a, b, Q;
+    __device__ RangeBounds(int64_t U, int Q_) : a(static_cast<int>(U) / Q_), b(static_cast<int>(U) % Q_), Q(Q_) {}
+    __device__ int start(int i) const { return a * i + (b * i) / Q; }
+};
+
 // The wavefronts whose ranges meet a row's blocks [rb0, rb1) of U: the row's
 // pieces come from wavefronts i0 .. i0 + n - 1.  Only the first can have
 // started its range in an earlier row (then this row is its second piece,
 // side0 = 1); every later one starts inside this row, so the row is its first
-// piece.
+// piece.  The first guesses (in floating point) are moved to the exact
+// wavefronts by the loops.
 __device__ __forceinline__ void row_pieces(const DecodeParams& p, int64_t U, int64_t rb0, int64_t rb1, int& i0, int& n,
                                            int& side0) {
     const int Q = effective_parts(U, p.parts);
-    i0 = static_cast<int>(rb0 * Q / U);
-    while (i0 + 1 < Q && range_start(U, i0 + 1, Q) <= rb0) ++i0;
-    while (i0 > 0 && range_start(U, i0, Q) > rb0) --i0;
-    int i1 = static_cast<int>((rb1 - 1) * Q / U);
-    while (i1 + 1 < Q && range_start(U, i1 + 1, Q) <= rb1 - 1) ++i1;
-    while (i1 > 0 && range_start(U, i1, Q) > rb1 - 1) --i1;
+    const RangeBounds rs(U, Q);
+    const float qu = static_cast<float>(Q) / static_cast<float>(U);
+    const int r0 = static_cast<int>(rb0), r1 = static_cast<int>(rb1) - 1;
+    i0 = min(max(static_cast<int>(static_cast<float>(r0) * qu), 0), Q - 1);
+    while (i0 + 1 < Q && rs.start(i0 + 1) <= r0) ++i0;
+    while (i0 > 0 && rs.start(i0) > r0) --i0;
+    int i1 = min(max(static_cast<int>(static_cast<float>(r1) * qu), 0), Q - 1);
+    while (i1 + 1 < Q && rs.start(i1 + 1) <= r1) ++i1;
+    while (i1 > 0 && rs.start(i1) > r1) --i1;
     n = i1 - i0 + 1;
-    side0 = range_start(U, i0, Q) < rb0 ? 1 : 0;
+    side0 = rs.start(i0) < r0 ? 1 : 0;
 }
 
 template <int QT>
@@ -897,19 +917,18 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
 // divided pieces in the slots - by the max/normaliser algebra of the online
 // softmax, in that order.  The prefix states carry no v_scale, the suffix
 // states do.  A row with no block past the prefix is its prefix states alone.
-// Same grid and lanes as decode_merge_kernel (one wavefront per row, kv head
-// and group of kMergeHeads query heads, which measured faster than one per
-// query head).
+// One wavefront per (row, kv head, group of kPrefixMergeHeads query heads),
+// kv head fastest, lanes as in decode_merge_kernel.
 template <int QT>
 __global__ __launch_bounds__(64) void decode_merge_prefix_kernel(const DecodeParams p) {
-    const int hgroups = (p.group + kMergeHeads - 1) / kMergeHeads;
+    const int hgroups = (p.group + kPrefixMergeHeads - 1) / kPrefixMergeHeads;
     const int kvh = static_cast<int>(blockIdx.x % p.hkv);
     const int rest = static_cast<int>(blockIdx.x / p.hkv);
-    const int h0 = (rest % hgroups) * kMergeHeads;
+    const int h0 = (rest % hgroups) * kPrefixMergeHeads;
     const int b = rest / hgroups;
     const int d = 2 * threadIdx.x;
     const int grp = p.group;
-    const int nh = min(kMergeHeads, grp - h0);
+    const int nh = min(kPrefixMergeHeads, grp - h0);
     if (!row_valid(p.kv_lens[b], p)) return;  // NaN from the plan
     const int64_t row_q = static_cast<int64_t>(b) * p.hq + kvh * grp;
     const int64_t U = p.plan[p.rows];
@@ -926,9 +945,9 @@ __global__ __launch_bounds__(64) void decode_merge_prefix_kernel(const DecodePar
     if (parts <= 2 && n <= 2) {
         // the usual case: every state of the wavefront's heads requested at
         // once (indices past the last repeat it and are left out)
-        float2 ml[kMergeHeads][4], ac[kMergeHeads][4];  // prefix ranges 0, 1, suffix pieces 0, 1
+        float2 ml[kPrefixMergeHeads][4], ac[kPrefixMergeHeads][4];  // prefix ranges 0, 1, suffix pieces 0, 1
 #pragma unroll
-        for (int a = 0; a < kMergeHeads; ++a) {
+        for (int a = 0; a < kPrefixMergeHeads; ++a) {
             const int hh = h0 + min(a, nh - 1);
             const float* ps = p.ws_prefix + (row_q + hh) * kPrefixState;
             const float* rs = p.ws_rows + (row_q + hh) * kPrefixState;
@@ -952,7 +971,7 @@ __global__ __launch_bounds__(64) void decode_merge_prefix_kernel(const DecodePar
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int a = 0; a < kMergeHeads; ++a) {
+        for (int a = 0; a < kPrefixMergeHeads; ++a) {
             if (a < nh) {
                 auto used = [&](int k) { return k < 2 ? k < parts : k - 2 < n; };
                 float mx = -INFINITY;
@@ -1175,7 +1194,8 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
             launch_decode_kernel<false>(c->kv_dtype, g1, stream, p);
     }
     mark(1);
-    const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + kMergeHeads - 1) / kMergeHeads;
+    const int heads = prefix ? kPrefixMergeHeads : kMergeHeads;
+    const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + heads - 1) / heads;
     const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads * hgroups));
     if (prefix)  // (bf16 queries: a shared prefix needs a bf16 or one-byte cache)
         hipLaunchKernelGGL(decode_merge_prefix_kernel<PKV_BF16>, mgrid, dim3(64), 0, stream, p);
