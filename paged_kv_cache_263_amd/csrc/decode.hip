@@ -765,7 +765,11 @@ __global__ __launch_bounds__(kFusedThreads, 2) void prefix_decode_kernel(const D
         pf::prefix_tile<KV>(pp, blockIdx.x, lds);
         return;
     }
-    const int w = threadIdx.x >> 6;
+    // The wavefront index, taken as wave-uniform: derived from threadIdx.x
+    // alone it counts as divergent, and every value computed from it (kv
+    // head, range, rows, block-table reads) would move to vector registers,
+    // the table reads becoming vector loads that wait for the tile in flight.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     unsigned char* mine = lds + w * DecodeLds<KV>::kBytes;
     decode_wave<KV, LOCAL_PLAN, QMEM, true>(p, (blockIdx.x - n_prefix) * 4 + w, threadIdx.x & 63,
                                             reinterpret_cast<int32_t*>(mine),
