@@ -170,12 +170,10 @@ struct Tile<PKV_BF16> {
     using Q = bf16x8_t[4];  // Q[head r][32 ks + 8 g .. +7]
     u32x4_t k[4];           // K[tok r][32 ks + 8 g .. +7]
     u32x2_t v[8];           // V^T[16 n + r][4 g .. 4 g + 3]
-    static __device__ __forceinline__ void load_q(Q& q, const void* qp, bool ok, int g) {
+    static __device__ __forceinline__ void load_q(Q& q, __amdgpu_buffer_rsrc_t qr, int qoff, int g) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t x = ok ? ld<u32x4_t>(static_cast<const uint16_t*>(qp) + 32 * ks + 8 * g) : u32x4_t{0, 0, 0, 0};
-            q[ks] = __builtin_bit_cast(bf16x8_t, x);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            q[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 64 * ks + 16 * g, 0, 0));
     }
     // Streaming (non-temporal) loads: a decode step reads each tile once, and
     // with this policy on both K and V the kernel reads the Llama-shaped
@@ -241,13 +239,11 @@ struct ByteTile {
     using Q = bf16x8_t[4];
     u32x4_t k[2];  // codes 64 s + 16 g .. +15 of token row r
     u32x4_t v[2];  // word n: tokens 4g..4g+3 of d row 16 n + r
-    static __device__ __forceinline__ void load_q(Q& q, const void* qp, bool ok, int g) {
+    static __device__ __forceinline__ void load_q(Q& q, __amdgpu_buffer_rsrc_t qr, int qoff, int g) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u32x4_t x = ok ? ld<u32x4_t>(static_cast<const uint16_t*>(qp) + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1))
-                           : u32x4_t{0, 0, 0, 0};
-            q[ks] = __builtin_bit_cast(bf16x8_t, x);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            q[ks] = __builtin_bit_cast(
+                bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 128 * (ks >> 1) + 32 * g + 16 * (ks & 1), 0, 0));
     }
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
 #pragma unroll
@@ -295,10 +291,10 @@ struct Tile<PKV_F32> {
     using Q = f32x4_t[8];  // Q[head r][32 g + 4 c .. +3]; k-step s = 4 c + i uses d = 32 g + s
     f32x4_t k[8];          // K[tok r][32 g + 4 c .. +3]
     f32x4_t v[8];          // V^T[16 n + r][4 g .. 4 g + 3]; k-step i uses token 4 g + i
-    static __device__ __forceinline__ void load_q(Q& q, const void* qp, bool ok, int g) {
+    static __device__ __forceinline__ void load_q(Q& q, __amdgpu_buffer_rsrc_t qr, int qoff, int g) {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-            q[c] = ok ? ld<f32x4_t>(static_cast<const float*>(qp) + 32 * g + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            q[c] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff + 128 * g + 16 * c, 0, 0));
     }
     __device__ __forceinline__ void load(const Elt* kt, const Elt* vt, int r, int g) {
 #pragma unroll
@@ -592,7 +588,20 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
     auto qrow_of = [&](int row) {
         return static_cast<int64_t>(row) * p.hq + kvh * p.group + (head_ok ? r : 0);
     };
-    auto q_ptr = [&](int row) { return static_cast<const char*>(p.q) + qrow_of(row) * kD * kQBytes; };
+    // The G query rows of kv head kvh in a row are contiguous; they are read
+    // through a per-row buffer descriptor (scalar base) with the lane's fixed
+    // offset, so no 64-bit vector address is computed in the loop (one placed
+    // in registers that an in-flight tile load targets would make the wave
+    // wait for that load).  Lanes past the G heads read past the descriptor's
+    // range, which returns zeros.
+    const int q_bytes = p.group * kD * kQBytes;
+    const int q_lane = head_ok ? r * kD * kQBytes : q_bytes;
+    auto q_rsrc = [&](int row) {
+        row = __builtin_amdgcn_readfirstlane(row);  // wave-uniform: scalar address arithmetic
+        return tile_rsrc(static_cast<const char*>(p.q) +
+                             (static_cast<int64_t>(row) * p.hq + kvh * p.group) * kD * kQBytes,
+                         q_bytes);
+    };
 
     // The wavefront's blocks u0 .. u1 - 1 (rows in order, each row's blocks
     // in order) stream through a ring of two register tiles: while block x is
@@ -633,7 +642,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
                 lrb1 = plan_at(bl + 1);
             } while (lrb1 <= x);
             l_len = clens[bl];
-            if constexpr (!QMEM) Tile<KV>::load_q(qn, q_ptr(bl), head_ok, g);  // requested before the tile, so waited for alone
+            if constexpr (!QMEM) Tile<KV>::load_q(qn, q_rsrc(bl), q_lane, g);  // requested before the tile, so waited for alone
             entered = true;
         }
         const int32_t id = ctable[static_cast<int64_t>(bl) * p.max_blocks + skip + (x - lrb0)];
@@ -653,7 +662,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
         issue(t[0], tbad[0], u0);
     } else {
         QReg q0;
-        Tile<KV>::load_q(q0, q_ptr(b_first), head_ok, g);
+        Tile<KV>::load_q(q0, q_rsrc(b_first), q_lane, g);
         issue(t[0], tbad[0], u0);
         q_store(0, q0);
     }
@@ -685,7 +694,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
             cslot = lslot;
         }
         QReg qm;
-        if constexpr (QMEM) Tile<KV>::load_q(qm, q_ptr(bc), head_ok, g);
+        if constexpr (QMEM) Tile<KV>::load_q(qm, q_rsrc(bc), q_lane, g);
         issue(nxt, nb, x + 1 < u1 ? x + 1 : u1 - 1);
         if (first) {
             piece_end = crb1 < u1 ? crb1 : u1;
