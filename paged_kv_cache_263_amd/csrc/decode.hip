@@ -65,6 +65,10 @@ namespace {
 // output [128], running max (log2 units), normaliser, 2 floats of padding
 // (16-byte aligned states).
 constexpr int kPrefixState = kD + 4;
+// what a finished piece of a row is written as: the output (the wavefront had
+// the whole row), the row's suffix state (whole row, shared prefix), or a piece
+// for the merge kernel
+constexpr int kRowOut = 0, kRowState = 1, kPiece = 2;
 
 struct DecodeParams {
     const void* q;                  // [rows][hq][128]
@@ -532,9 +536,9 @@ struct DecodeLds {  // LDS of one decode wavefront: its plan (if it builds one) 
 // wavefront per workgroup in decode_kernel; four per workgroup, after the
 // shared-prefix pass's workgroups, in prefix_decode_kernel), plan_sh and q_sh
 // its LDS.
-template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX>
+template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX, bool STASH>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, int lane, int32_t* plan_sh,
-                                            u32x4_t* q_sh) {
+                                            u32x4_t* q_sh, float* stash, int stash_bytes) {
     constexpr int QT = (KV == PKV_F32) ? PKV_F32 : PKV_BF16;
     constexpr int kQBytes = (QT == PKV_F32) ? 4 : 2;
     using Elt = typename Tile<KV>::Elt;
@@ -585,9 +589,6 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
     const Elt* kpool = static_cast<const Elt*>(p.k_pool) + static_cast<int64_t>(kvh) * kTile;
     const Elt* vpool = static_cast<const Elt*>(p.v_pool) + static_cast<int64_t>(kvh) * kTile;
     const int64_t blk_stride = static_cast<int64_t>(p.hkv) * kTile;
-    auto qrow_of = [&](int row) {
-        return static_cast<int64_t>(row) * p.hq + kvh * p.group + (head_ok ? r : 0);
-    };
     // The G query rows of kv head kvh in a row are contiguous; they are read
     // through a per-row buffer descriptor (scalar base) with the lane's fixed
     // offset, so no 64-bit vector address is computed in the loop (one placed
@@ -678,6 +679,58 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
     int t1 = 0;
     bool pbad = false;
     Online o;
+    // Results of finished pieces.  A global store counts in the same in-order
+    // counter as the tile loads, so every later wait for a tile would also
+    // wait for the store to complete; the results are therefore kept in this
+    // wavefront's LDS (the stash: per entry its kind and destination, then the
+    // values of the G heads' lanes) and written when the range is done, or
+    // earlier when the stash is full.
+    const int ent_floats = (4 + 130 * p.group + 3) / 4 * 4;
+    const int cap = STASH ? stash_bytes / (ent_floats * 4) : 0;
+    const int li = g * p.group + r;  // the lane's place in an entry (lanes with head_ok)
+    int nst = 0;
+    auto write = [&](int kind, int64_t base, const f32x4_t v[8], float2 ml) {
+        if (!head_ok) return;
+        const int64_t row = base + r;
+        if (kind == kRowOut) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n) store_out4<QT>(p.out, row, 16 * n + 4 * g, v[n]);
+        } else {
+            float* a = kind == kRowState ? p.ws_rows + row * kPrefixState : p.ws_acc + row * kD;
+            float* m = kind == kRowState ? a + kD : p.ws_ml + 2 * row;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) st<f32x4_t>(a + 16 * n + 4 * g, v[n]);
+            if (g == 0) st<float2>(m, ml);
+        }
+    };
+    auto put = [&](int e, int kind, int64_t base, const f32x4_t v[8], float2 ml) {
+        float* ent = stash + e * ent_floats;
+        if (lane == 0)
+            *reinterpret_cast<int4*>(ent) =
+                int4{kind, static_cast<int>(base & 0xFFFFFFFF), static_cast<int>(base >> 32), 0};
+        if (head_ok) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4_t*>(ent + 4 + 32 * li + 4 * n) = v[n];
+            if (g == 0) *reinterpret_cast<float2*>(ent + 4 + 128 * p.group + 2 * r) = ml;
+        }
+    };
+    auto flush = [&] {
+        for (int e = 0; e < nst; ++e) {
+            const float* ent = stash + e * ent_floats;
+            const int4 meta = *reinterpret_cast<const int4*>(ent);
+            const int kind = __builtin_amdgcn_readfirstlane(meta.x);
+            const int64_t base = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(meta.z)) << 32) |
+                                 static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(meta.y));
+            f32x4_t v[8];
+            float2 ml = {0.f, 0.f};
+            if (head_ok) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) v[n] = *reinterpret_cast<const f32x4_t*>(ent + 4 + 32 * li + 4 * n);
+                if (g == 0) ml = *reinterpret_cast<const float2*>(ent + 4 + 128 * p.group + 2 * r);
+            }
+            write(kind, base, v, ml);
+        }
+    };
     // One block x: computed from `cur` while block x + 1 (the range's last
     // block again at its end: a cache hit, never used) loads into `nxt`.  A
     // new row takes over the load cursor's query slot before that load, which
@@ -712,13 +765,32 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
             q_fetch(cslot, q);
         }
         o.step<KV>(cur, q, scale, tok0 + 4 * g, t1, tok0 + kBS);
-        if (x + 1 == piece_end) {  // last block of the piece: write it
+        if (x + 1 == piece_end) {  // last block of the piece: its result
             float l = o.l;
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
             const bool whole = crb0 >= u0 && crb1 <= u1;  // no other wavefront touches this row
-            if (head_ok) {
-                const int64_t qrow = qrow_of(bc);
+            if constexpr (STASH) {
+                const int kind = whole ? (PREFIX ? kRowState : kRowOut) : kPiece;
+                const int64_t base = whole ? static_cast<int64_t>(bc) * p.hq + kvh * p.group
+                                           : ((static_cast<int64_t>(kvh) * p.parts + wi) * 2 +
+                                              (bc == b_first ? 0 : 1)) * p.group;
+                f32x4_t v[8];
+                const float f = kind == kRowOut ? (pbad ? nan : vs / l) : vs;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) v[n] = (pbad && kind != kRowOut) ? nan4 : o.acc[n] * f;
+                const float2 ml = {o.m, pbad ? nan : l};
+                if (cap > 0) {
+                    if (nst == cap) {
+                        flush();
+                        nst = 0;
+                    }
+                    put(nst++, kind, base, v, ml);
+                } else {
+                    write(kind, base, v, ml);
+                }
+            } else if (head_ok) {  // written at once
+                const int64_t qrow = static_cast<int64_t>(bc) * p.hq + kvh * p.group + r;
                 if (whole && PREFIX) {
                     float* sp = p.ws_rows + qrow * kPrefixState;
 #pragma unroll
@@ -746,13 +818,25 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
         if (x + 1 >= u1) break;
         step(t[1], tbad[1], t[0], tbad[0], x + 1);
     }
+    if constexpr (STASH) flush();
 }
+
+// Stash bytes of a decode_kernel wavefront: with the plan and query slots,
+// the LDS of the four bf16 workgroups a compute unit holds at the default
+// partition stays well within its 160 KB.  One-byte caches (eight workgroups
+// per CU, long rows with one or two pieces per wavefront) write directly:
+// their stash measured slower (fp8 long context 658 against 653 us).
+template <int KV, bool QMEM>
+constexpr int kStashBytes = KV == PKV_BF16 ? (QMEM ? 24576 : 16384) : 0;
 
 template <int KV, bool LOCAL_PLAN, bool QMEM>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
     __shared__ int32_t plan_sh[LOCAL_PLAN ? kLocalPlanRows + 1 : 1];
     __shared__ u32x4_t q_sh[DecodeLds<KV>::kQSlots];
-    decode_wave<KV, LOCAL_PLAN, QMEM, false>(p, blockIdx.x, threadIdx.x, plan_sh, q_sh);
+    __shared__ f32x4_t stash[kStashBytes<KV, QMEM> > 0 ? kStashBytes<KV, QMEM> / 16 : 1];
+    decode_wave<KV, LOCAL_PLAN, QMEM, false, (kStashBytes<KV, QMEM> > 0)>(p, blockIdx.x, threadIdx.x, plan_sh, q_sh,
+                                             kStashBytes<KV, QMEM> > 0 ? reinterpret_cast<float*>(stash) : nullptr,
+                                             kStashBytes<KV, QMEM>);
 }
 
 // A decode call with a shared prefix, in one launch: workgroups 0 ..
@@ -768,7 +852,8 @@ constexpr int kFusedLds = pf::kPrefixLdsBytes;
 template <int KV, bool LOCAL_PLAN, bool QMEM>
 __global__ __launch_bounds__(kFusedThreads, 2) void prefix_decode_kernel(const DecodeParams p, const pf::PrefillParams pp,
                                                                          int n_prefix) {
-    static_assert(4 * DecodeLds<KV>::kBytes <= kFusedLds, "four decode wavefronts fit the pass's LDS");
+    constexpr int kWaveLds = kFusedLds / 4 / 16 * 16;  // each decode wavefront's share: plan, query slots, stash
+    static_assert(DecodeLds<KV>::kBytes < kWaveLds, "four decode wavefronts fit the pass's LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[kFusedLds];
     if (static_cast<int>(blockIdx.x) < n_prefix) {
         pf::prefix_tile<KV>(pp, blockIdx.x, lds);
@@ -779,10 +864,12 @@ __global__ __launch_bounds__(kFusedThreads, 2) void prefix_decode_kernel(const D
     // head, range, rows, block-table reads) would move to vector registers,
     // the table reads becoming vector loads that wait for the tile in flight.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    unsigned char* mine = lds + w * DecodeLds<KV>::kBytes;
-    decode_wave<KV, LOCAL_PLAN, QMEM, true>(p, (blockIdx.x - n_prefix) * 4 + w, threadIdx.x & 63,
+    unsigned char* mine = lds + w * kWaveLds;
+    decode_wave<KV, LOCAL_PLAN, QMEM, true, KV == PKV_BF16>(p, (blockIdx.x - n_prefix) * 4 + w, threadIdx.x & 63,
                                             reinterpret_cast<int32_t*>(mine),
-                                            reinterpret_cast<u32x4_t*>(mine + DecodeLds<KV>::kPlanInts * 4));
+                                            reinterpret_cast<u32x4_t*>(mine + DecodeLds<KV>::kPlanInts * 4),
+                                            reinterpret_cast<float*>(mine + DecodeLds<KV>::kBytes),
+                                            kWaveLds - DecodeLds<KV>::kBytes);
 }
 
 // Merge the pieces of one (row, query head) that was divided between
