@@ -274,14 +274,17 @@ def test_invalid_rows_give_nan_and_others_stay_right():
     del good
 
 
-@pytest.mark.parametrize("kv,hq,hkv", [("bf16", 16, 2), ("bf16", 8, 2), ("fp8", 16, 2), ("f32", 8, 2)])
+@pytest.mark.parametrize("kv,hq,hkv", [("bf16", 16, 2), ("bf16", 8, 2), ("bf16", 32, 2), ("fp8", 16, 2), ("f32", 8, 2)])
 def test_runs_of_short_rows(kv, hq, hkv):
     """Rows of one to three blocks in a run: a wavefront enters a new row at
     nearly every block, so each row's query must reach the compute side in
     order (handed over through a slot per row, or re-read from memory at
-    every block for bf16 with four query heads per kv head) while the next
-    row's query is already being fetched.  One wavefront per kv head walks every
-    row; other partitions cut the run in different places.  Empty rows in
+    every block for bf16 with up to eight query heads per kv head) while the
+    next row's query is already being fetched.  One wavefront per kv head
+    walks every row; other partitions cut the run in different places.  With
+    bf16 the finished rows go through the wavefront's LDS stash, which fills
+    many times over here (one entry at sixteen query heads per kv head, five
+    at eight, eleven at four) and is written out each time.  Empty rows in
     the run (length 0) get NaN and are skipped without disturbing the
     hand-over of their neighbours."""
     import paged_kv_cache_263_amd as pk
