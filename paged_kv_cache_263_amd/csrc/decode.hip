@@ -535,7 +535,8 @@ struct DecodeLds {  // LDS of one decode wavefront: its plan (if it builds one) 
 // One wavefront of the decode grid: vblock is its index in the grid (one
 // wavefront per workgroup in decode_kernel; four per workgroup, after the
 // shared-prefix pass's workgroups, in prefix_decode_kernel), plan_sh and q_sh
-// its LDS.
+// its LDS; with STASH, stash (stash_bytes of LDS) holds its finished pieces
+// until its range is done.
 template <int KV, bool LOCAL_PLAN, bool QMEM, bool PREFIX, bool STASH>
 __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, int lane, int32_t* plan_sh,
                                             u32x4_t* q_sh, float* stash, int stash_bytes) {
@@ -859,15 +860,15 @@ __global__ __launch_bounds__(kFusedThreads, 2) void prefix_decode_kernel(const D
         pf::prefix_tile<KV>(pp, blockIdx.x, lds);
         return;
     }
-    // The wavefront index, taken as wave-uniform: derived from threadIdx.x
-    // alone it counts as divergent, and every value computed from it (kv
-    // head, range, rows, block-table reads) would move to vector registers,
-    // the table reads becoming vector loads that wait for the tile in flight.
     // The decode wavefronts issue at the highest wave priority: on a compute
     // unit they share with a pass workgroup, their loads are then issued
     // ahead of the pass's arithmetic (prefix pass + decode on the 256-row
     // batch: 119.8 against 123.2 us event-timed; priority 1: 120.2 us).
     __builtin_amdgcn_s_setprio(3);
+    // The wavefront index, taken as wave-uniform: derived from threadIdx.x
+    // alone it counts as divergent, and every value computed from it (kv
+    // head, range, rows, block-table reads) would move to vector registers,
+    // the table reads becoming vector loads that wait for the tile in flight.
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     unsigned char* mine = lds + w * kWaveLds;
     decode_wave<KV, LOCAL_PLAN, QMEM, true, KV == PKV_BF16>(p, (blockIdx.x - n_prefix) * 4 + w, threadIdx.x & 63,
