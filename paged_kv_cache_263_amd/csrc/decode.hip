@@ -82,6 +82,11 @@ struct DecodeParams {
     int32_t* plan;                  // [rows + 1]: blocks of rows 0..b-1 (0 blocks for an invalid row)
     float* ws_acc;                  // [hkv][Q][2][group][128] partial unnormalised outputs
     float* ws_ml;                   // [hkv][Q][2][group][2] partial (max, normaliser)
+    // [hkv][Q] per decode wavefront: {row, its first block, one past its
+    // last, U} of the row whose first block is in the wavefront's range and
+    // that another wavefront continues, else row -1 (no prefix)
+    int4* ws_cut;
+    int32_t merge_owners;           // the merge kernel's grid runs over wavefronts (ws_cut), not rows
     const float* ws_prefix;         // shared prefix: [parts][rows][hq][kPrefixState] (acc[128], max, normaliser)
     int32_t prefix_blocks;          // S: every row's table starts with the same S blocks (0 = none)
     int32_t prefix_parts;           // key ranges the prefix states were computed over
@@ -820,6 +825,13 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
         step(t[1], tbad[1], t[0], tbad[0], x + 1);
     }
     if constexpr (STASH) flush();
+    if constexpr (!PREFIX) {
+        // the row this wavefront began and another one continues (at most
+        // one: the last row of the range), for the merge kernel
+        if (lane == 0)
+            p.ws_cut[static_cast<int64_t>(kvh) * p.parts + wi] =
+                (crb0 >= u0 && crb1 > u1) ? make_int4(bc, crb0, crb1, U) : make_int4(-1, 0, 0, 0);
+    }
 }
 
 // Stash bytes of a decode_kernel wavefront: with the plan and query slots,
@@ -894,6 +906,16 @@ constexpr int kMergeBatch = 8;
 // batch spilled scalar registers; fp8 long context 7.5 against 16.6 us); the
 // shared-prefix merge, with few pieces per row, is fastest at four
 // (kPrefixMergeHeads: 10.2 against 15.5 us at one).
+// With more rows than wavefronts per kv head, most rows are whole, and a
+// wavefront per row and head costs more than the merging itself: the merge
+// then runs one wavefront per (decode wavefront, kv head, head group), which
+// merges the row that decode wavefront began and another continued, if any
+// (recorded by the decode kernel; a row divided between wavefronts has
+// exactly one such owner).  Measured per decode call (decode + merge), eight
+// query heads per kv head: 1024 rows of 132 tokens 139.6 -> 116.3 us, 512 of
+// 264 108.6 -> 96.1, 256 of 528 95.1 -> 90.1.  Wavefronts per workgroup do
+// not matter: four or more per workgroup changed nothing, the count of
+// wavefronts does.
 constexpr int kMergeHeads = 1;
 constexpr int kPrefixMergeHeads = 4;
 
@@ -947,15 +969,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeParams p) 
     const int kvh = static_cast<int>(blockIdx.x % p.hkv);
     const int rest = static_cast<int>(blockIdx.x / p.hkv);
     const int h0 = (rest % hgroups) * kMergeHeads;
-    const int b = rest / hgroups;
     const int d = 2 * threadIdx.x;
     const int grp = p.group;
     const int nh = min(kMergeHeads, grp - h0);  // heads of this wavefront
+    int b;
+    int64_t U, rb0, rb1;
+    if (p.merge_owners) {
+        // rest / hgroups is a decode wavefront: the row it began that another
+        // continues, if any (the records of wavefronts past the effective
+        // count are left from earlier calls)
+        const int i = rest / hgroups;
+        const int4 cut = p.ws_cut[static_cast<int64_t>(kvh) * p.parts + i];
+        U = p.plan[p.rows];
+        if (U <= 0 || i >= effective_parts(U, p.parts) || cut.x < 0) return;
+        b = cut.x;
+        rb0 = cut.y;
+        rb1 = cut.z;
+    } else {
+        b = rest / hgroups;
+        U = p.plan[p.rows];
+        rb0 = p.plan[b];
+        rb1 = p.plan[b + 1];
+        if (rb1 <= rb0 || U <= 0) return;  // an invalid row (NaN from the plan)
+    }
     const int64_t row_q = static_cast<int64_t>(b) * p.hq + kvh * grp;  // query row of head 0 of the group
-    const int64_t U = p.plan[p.rows];
-    const int64_t rb0 = p.plan[b];
-    const int64_t rb1 = p.plan[b + 1];
-    if (rb1 <= rb0 || U <= 0) return;  // an invalid row (NaN from the plan)
     int i0, n, side0;
     row_pieces(p, U, rb0, rb1, i0, n, side0);
     if (n == 1) return;  // written directly by the one wavefront
@@ -1215,11 +1252,12 @@ size_t decode_workspace_bytes(const pkv_cache* c, const pkv_attn_args* a, int32_
     const int64_t group = a->num_q_heads / c->num_kv_heads;
     const int64_t plan = (static_cast<int64_t>(rows) + 1 + 3) / 4 * 4;  // int32, 16-byte multiple
     const int64_t slots = static_cast<int64_t>(c->num_kv_heads) * Q * 2 * group;
+    const int64_t cuts = static_cast<int64_t>(c->num_kv_heads) * Q;  // int4 each
     // shared prefix: the states of its key ranges, then the rows' suffix states
     const int64_t prefix = a->shared_prefix_blocks > 0 ? (static_cast<int64_t>(prefix_parts(c, a, rows)) + 1) * rows *
                                                              a->num_q_heads * kPrefixState
                                                        : 0;
-    return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4 + prefix * 4);
+    return static_cast<size_t>(plan * 4 + slots * (kD + 2) * 4 + cuts * 16 + prefix * 4);
 }
 
 // Launch decode over `rows` rows whose q/out/table/kv_lens start at the given
@@ -1256,9 +1294,12 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     p.plan = static_cast<int32_t*>(workspace);
     p.ws_acc = reinterpret_cast<float*>(static_cast<int32_t*>(workspace) + plan_ints);
     p.ws_ml = p.ws_acc + slots * kD;
+    p.ws_cut = reinterpret_cast<int4*>(p.ws_ml + slots * 2);  // 16-byte aligned: slots is even
     p.prefix_blocks = a->shared_prefix_blocks;
     p.prefix_parts = a->shared_prefix_blocks > 0 ? prefix_parts(c, a, rows) : 0;
-    p.ws_prefix = a->shared_prefix_blocks > 0 ? p.ws_ml + slots * 2 : nullptr;
+    p.ws_prefix = a->shared_prefix_blocks > 0
+                      ? reinterpret_cast<float*>(p.ws_cut + static_cast<int64_t>(c->num_kv_heads) * Q)
+                      : nullptr;
     p.ws_rows = a->shared_prefix_blocks > 0
                     ? const_cast<float*>(p.ws_prefix) + static_cast<int64_t>(p.prefix_parts) * rows * a->num_q_heads *
                                                             kPrefixState
@@ -1302,7 +1343,13 @@ int launch_decode(const pkv_cache* c, const pkv_attn_args* a, int32_t rows, int3
     mark(1);
     const int heads = prefix ? kPrefixMergeHeads : kMergeHeads;
     const int64_t hgroups = (a->num_q_heads / c->num_kv_heads + heads - 1) / heads;
-    const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(rows) * c->num_kv_heads * hgroups));
+    // Without a prefix only rows divided between wavefronts need merging, and
+    // each has one owner (the wavefront holding its first block); with more
+    // rows than wavefronts per kv head the grid runs over the wavefronts'
+    // owner records instead of the rows.
+    p.merge_owners = !prefix && rows > Q ? 1 : 0;
+    const int64_t units = p.merge_owners ? Q : rows;
+    const dim3 mgrid(static_cast<unsigned>(units * c->num_kv_heads * hgroups));
     if (prefix)  // (bf16 queries: a shared prefix needs a bf16 or one-byte cache)
         hipLaunchKernelGGL(decode_merge_prefix_kernel<PKV_BF16>, mgrid, dim3(64), 0, stream, p);
     else if (f32)
