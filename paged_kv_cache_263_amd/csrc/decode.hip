@@ -41,7 +41,9 @@
 // finished and written by that wavefront; a row cut by range boundaries is
 // left as partial results (running max, normaliser, unnormalised output) -
 // at most two per wavefront, one for the row at each end of its range - and
-// the merge kernel combines them in wavefront order.  The partition depends
+// the merge kernel combines them in wavefront order (over the rows, or, with
+// more rows than wavefronts per kv head, over the wavefronts' records of the
+// divided rows they began).  The partition depends
 // on the lengths only, so every sum is taken in an order fixed by logical
 // positions and a permutation of the physical blocks changes no bit of the
 // output.
