@@ -85,8 +85,8 @@ struct DecodeParams {
     float* ws_acc;                  // [hkv][Q][2][group][128] partial unnormalised outputs
     float* ws_ml;                   // [hkv][Q][2][group][2] partial (max, normaliser)
     // [hkv][Q] per decode wavefront: {row, its first block, one past its
-    // last, U} of the row whose first block is in the wavefront's range and
-    // that another wavefront continues, else row -1 (no prefix)
+    // last block, 0} of the row whose first block is in the wavefront's range
+    // and that another wavefront continues, else row -1 (no prefix)
     int4* ws_cut;
     int32_t merge_owners;           // the merge kernel's grid runs over wavefronts (ws_cut), not rows
     const float* ws_prefix;         // shared prefix: [parts][rows][hq][kPrefixState] (acc[128], max, normaliser)
@@ -832,7 +832,7 @@ __device__ __forceinline__ void decode_wave(const DecodeParams& p, int vblock, i
         // one: the last row of the range), for the merge kernel
         if (lane == 0)
             p.ws_cut[static_cast<int64_t>(kvh) * p.parts + wi] =
-                (crb0 >= u0 && crb1 > u1) ? make_int4(bc, crb0, crb1, U) : make_int4(-1, 0, 0, 0);
+                (crb0 >= u0 && crb1 > u1) ? make_int4(bc, crb0, crb1, 0) : make_int4(-1, 0, 0, 0);
     }
 }
 
